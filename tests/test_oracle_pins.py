@@ -1,0 +1,452 @@
+"""Pins of the CPU oracle to things other than itself: hand-derived values,
+closed forms, exhaustive enumeration, invariants, and special cases that
+reduce to a library routine.  No GPU involved."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import load_golden
+
+
+def _hand_layer(kind):
+    g = load_golden("hand_ffn.json")
+    s = g[kind]
+    f64 = lambda v: np.asarray(v, dtype=np.float32)  # noqa: E731  small integers/halves are exact
+    L = dict(kind=kind, w_dtype="f32", p_dtype="f32", d=3, d_ffn=4, r=2,
+             w_gate=f64(s["w_gate"]) if kind == "reglu" else None, w_up=f64(s["w_up"]),
+             w_down_t=f64(s["w_down_t"]), b_act=f64(s["b_act"]),
+             p_w1=f64(g["predictor"]["p_w1"]), p_b1=f64(g["predictor"]["p_b1"]),
+             p_w2=f64(g["predictor"]["p_w2"]), p_b2=f64(g["predictor"]["p_b2"]), t=0.0)
+    return L, np.asarray(g["x"], np.float64), s, g["predictor"]
+
+
+def _rand_layer(rng, kind, d, d_ffn, r=8, w_dtype="f32", density=0.3):
+    """Small random layer; biases put about `density` of the neurons above zero."""
+    def mat(rows, cols):
+        w = rng.standard_normal((rows, cols)) / math.sqrt(cols)
+        return w.astype(np.float16 if w_dtype == "f16" else np.float32)
+    L = dict(kind=kind, w_dtype=w_dtype, p_dtype=w_dtype, d=d, d_ffn=d_ffn, r=r,
+             w_gate=mat(d_ffn, d) if kind == "reglu" else None, w_up=mat(d_ffn, d),
+             w_down_t=mat(d_ffn, d),
+             b_act=(rng.standard_normal(d_ffn) * 0.3 - 0.5 * (1 - density)).astype(np.float32),
+             p_w1=mat(r, d), p_b1=np.zeros(r, np.float32), p_w2=mat(d_ffn, r),
+             p_b2=(rng.standard_normal(d_ffn) * 0.1).astype(np.float32), t=0.0)
+    return L
+
+
+# --------------------------------------------------------------------------- #
+# element formats
+# --------------------------------------------------------------------------- #
+def test_f16_decode_all_bit_patterns():
+    """Every binary16 pattern against numpy's float16 -> float64 widening."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.f16_bits_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert math.copysign(1.0, ours[0x8000]) == -1.0
+
+
+def test_q4_0_block_hand_values():
+    """One block with scale 0.5 (fp16 0x3800): code k in the low nibble of
+    byte k, code k+16 in the high nibble; value (code - 8) * scale."""
+    codes = np.array([(k * 7 + 3) % 16 for k in range(32)], dtype=np.uint8)
+    blk = np.zeros(18, np.uint8)
+    blk[0], blk[1] = 0x00, 0x38
+    for k in range(16):
+        blk[2 + k] = codes[k] | (codes[k + 16] << 4)
+    vals = oracle.deq(blk[None, :], "q4_0", 32)[0]
+    assert np.array_equal(vals, (codes.astype(np.float64) - 8.0) * 0.5)
+    # the three anchor codes
+    blk2 = blk.copy()
+    blk2[2] = 0x80 | 0x00     # code 0 -> 0, code 16 -> 8
+    blk2[3] = 0x0F            # code 1 -> 15, code 17 -> 0
+    v2 = oracle.deq(blk2[None, :], "q4_0", 32)[0]
+    assert v2[0] == -8 * 0.5 and v2[16] == 0.0 and v2[1] == 7 * 0.5 and v2[17] == -8 * 0.5
+
+
+def test_q4_0_zero_scale_and_rows():
+    rng = np.random.default_rng(1)
+    rows, cols = 3, 64
+    blocks = rng.integers(0, 256, size=(rows, cols // 32, 18), dtype=np.uint8)
+    blocks[1, 0, 0:2] = 0  # zero scale -> all zero (both signs of zero allowed)
+    vals = oracle.deq(blocks.reshape(rows, -1), "q4_0", cols)
+    assert np.all(vals[1, :32] == 0.0)
+    for i in range(rows):
+        for b in range(cols // 32):
+            s = np.frombuffer(blocks[i, b, 0:2].tobytes(), dtype="<f2")[0].astype(np.float64)
+            q = np.concatenate([blocks[i, b, 2:] & 15, blocks[i, b, 2:] >> 4]).astype(np.float64)
+            exp = (q - 8.0) * s
+            got = vals[i, b * 32:(b + 1) * 32]
+            fin = np.isfinite(exp)
+            assert np.array_equal(got[fin], exp[fin])
+
+
+# --------------------------------------------------------------------------- #
+# hand example: FFN and predictor
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_hand_ffn(kind):
+    L, x, s, _ = _hand_layer(kind)
+    y, act = oracle.ffn_dense(L, x)
+    assert y.tolist() == s["y"]
+    assert act.tolist() == s["act"]
+    z, u, m = oracle.preact(L, x)
+    assert z.tolist() == s["z"]
+    assert m.tolist() == s["exact_mask"]
+    if kind == "reglu":
+        assert u.tolist() == s["u"]
+    assert oracle.ffn_masked(L, x, m).tolist() == s["y"]
+    ys, acts = oracle.ffn_sparse(L, x, oracle.compact(m))
+    assert ys.tolist() == s["y"]
+    assert acts.tolist() == [a for a, mm in zip(s["act"], s["exact_mask"]) if mm]
+
+
+def test_hand_predictor():
+    L, x, _, p = _hand_layer("relu")
+    hid, logits, mask = oracle.predict(L, x)
+    assert hid.tolist() == p["hid"]
+    assert logits.tolist() == p["logits"]
+    assert mask.tolist() == p["mask_tau_0.5"]
+    L6 = dict(L, t=oracle.logit_threshold(0.6))
+    assert oracle.predict(L6, x)[2].tolist() == p["mask_tau_0.6"]
+
+
+# --------------------------------------------------------------------------- #
+# threshold
+# --------------------------------------------------------------------------- #
+def test_threshold_equals_sigmoid_rule():
+    """logit > ln(tau/(1-tau)) selects the same neurons as sigmoid(logit) > tau
+    away from the boundary; at exactly t the neuron is inactive."""
+    rng = np.random.default_rng(2)
+    lg = (rng.standard_normal(20000) * 4).astype(np.float32)
+    for tau in (0.3, 0.45, 0.5, 0.6, 0.9):
+        t = oracle.logit_threshold(tau)
+        m = oracle.threshold(lg, t)
+        sig = 1.0 / (1.0 + np.exp(-lg.astype(np.float64)))
+        far = np.abs(lg.astype(np.float64) - t) > 1e-6
+        assert np.array_equal(m[far], (sig > tau)[far].astype(np.uint8))
+    assert oracle.threshold(np.array([0.0, -0.0, 1e-45, -1e-45], np.float32), 0.0).tolist() == \
+        [0, 0, 1, 0]
+    assert oracle.logit_threshold(0.5) == 0.0
+    assert oracle.threshold(np.array([np.nan], np.float32), 0.0).tolist() == [0]
+
+
+def test_predictor_linear_special_case():
+    """W1 = I, b1 = 0 and x >= 0 make the hidden layer the identity, so the
+    logits are the affine map W2 x + b2 (numpy matmul)."""
+    rng = np.random.default_rng(3)
+    d = r = 16
+    F = 40
+    x = rng.random(d)
+    L = dict(d=d, d_ffn=F, r=r, p_dtype="f32", p_w1=np.eye(d, dtype=np.float32),
+             p_b1=np.zeros(r, np.float32), p_w2=rng.standard_normal((F, r)).astype(np.float32),
+             p_b2=rng.standard_normal(F).astype(np.float32), t=0.0)
+    hid, logits, mask = oracle.predict(L, x)
+    assert np.array_equal(hid, x)
+    ref = L["p_w2"].astype(np.float64) @ x + L["p_b2"]
+    np.testing.assert_allclose(logits, ref, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(mask, (ref > 0).astype(np.uint8))
+
+
+def test_predictor_hidden_relu_kills_negative_units():
+    """With W2 reading only hidden units whose pre-activation is negative, every
+    logit equals its bias."""
+    d, r, F = 4, 2, 3
+    L = dict(d=d, d_ffn=F, r=r, p_dtype="f32",
+             p_w1=np.array([[1, 0, 0, 0], [-1, 0, 0, 0]], np.float32),
+             p_b1=np.zeros(r, np.float32),
+             p_w2=np.array([[0, 7], [0, -3], [0, 1]], np.float32),
+             p_b2=np.array([0.5, -0.5, 0.0], np.float32), t=0.0)
+    hid, logits, mask = oracle.predict(L, np.array([2.0, 1, 1, 1]))
+    assert hid.tolist() == [2.0, 0.0]
+    assert logits.tolist() == [0.5, -0.5, 0.0]
+    assert mask.tolist() == [1, 0, 0]
+
+
+# --------------------------------------------------------------------------- #
+# compaction and union
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("n", [0, 1, 5, 12, 16])
+def test_compact_exhaustive(n):
+    for bits in range(1 << n):
+        m = np.array([(bits >> i) & 1 for i in range(n)], dtype=np.uint8)
+        idx = oracle.compact(m)
+        assert np.array_equal(idx, np.flatnonzero(m))
+        if n and bits in (0, (1 << n) - 1):
+            assert idx.size == (0 if bits == 0 else n)
+
+
+def test_compact_random_large():
+    rng = np.random.default_rng(4)
+    for n in (100_000, 28672, 49152):
+        for p in (0.0, 0.01, 0.1, 0.5, 1.0):
+            m = (rng.random(n) < p).astype(np.uint8)
+            m[m == 1] = rng.integers(1, 256, size=int(m.sum()), dtype=np.uint8)  # any nonzero
+            idx = oracle.compact(m)
+            assert idx.dtype == np.int32
+            assert idx.size == np.count_nonzero(m)
+            assert np.all(np.diff(idx) > 0)
+            assert np.array_equal(idx, np.flatnonzero(m))
+
+
+def test_union():
+    rng = np.random.default_rng(5)
+    for B in (1, 2, 4, 16):
+        masks = (rng.random((B, 300)) < 0.1).astype(np.uint8)
+        U = oracle.union(masks)
+        assert np.array_equal(U, masks.any(axis=0).astype(np.uint8))
+        assert U.sum() >= masks.sum(axis=1).max()
+        if B == 1:
+            assert np.array_equal(U, masks[0])
+    # exhaustive over two 3-bit masks
+    for a, b in itertools.product(range(8), repeat=2):
+        m = np.array([[(a >> i) & 1 for i in range(3)], [(b >> i) & 1 for i in range(3)]],
+                     np.uint8)
+        assert oracle.union(m).tolist() == [((a | b) >> i) & 1 for i in range(3)]
+
+
+# --------------------------------------------------------------------------- #
+# FFN invariants and special cases
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+@pytest.mark.parametrize("w_dtype", ["f32", "f16"])
+def test_exact_mask_and_all_ones_equal_dense(kind, w_dtype):
+    """Sparse FFN on the exact mask (z > 0) and on the all-ones mask equal the
+    dense FFN exactly: the skipped terms are exact zeros."""
+    rng = np.random.default_rng(6)
+    L = _rand_layer(rng, kind, 24, 70, w_dtype=w_dtype)
+    for _ in range(5):
+        x = rng.standard_normal(24)
+        y, act = oracle.ffn_dense(L, x)
+        _, _, em = oracle.preact(L, x)
+        assert 0 < em.sum() < 70
+        assert np.array_equal(oracle.ffn_masked(L, x, em), y)
+        assert np.array_equal(oracle.ffn_masked(L, x, np.ones(70, np.uint8)), y)
+        assert np.all(act[em == 0] == 0)
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_predicted_mask_equals_dense_with_zeroed_neurons(kind):
+    """Sparse FFN on the predictor's mask equals the dense FFN of the same layer
+    with the down column of every non-predicted neuron set to zero."""
+    rng = np.random.default_rng(7)
+    L = _rand_layer(rng, kind, 20, 50, r=6)
+    for _ in range(5):
+        x = rng.standard_normal(20)
+        _, _, pm = oracle.predict(L, x)
+        Lz = dict(L, w_down_t=L["w_down_t"] * pm[:, None].astype(np.float32))
+        assert np.array_equal(oracle.ffn_masked(L, x, pm), oracle.ffn_dense(Lz, x)[0])
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_masked_ffn_brute_force_all_masks(kind):
+    """For every one of the 2^10 masks, the masked FFN is the sum of the
+    single-neuron FFNs it contains, and a single neuron i gives
+    a_i * W_downT[i] with a_i from the closed form."""
+    rng = np.random.default_rng(8)
+    d, F = 5, 10
+    L = _rand_layer(rng, kind, d, F)
+    x = rng.standard_normal(d)
+    wu = L["w_up"].astype(np.float64)
+    wd = L["w_down_t"].astype(np.float64)
+    b = L["b_act"].astype(np.float64)
+    single = []
+    for i in range(F):
+        if kind == "relu":
+            a = max(float(wu[i] @ x + b[i]), 0.0)
+        else:
+            a = max(float(L["w_gate"][i].astype(np.float64) @ x + b[i]), 0.0) * float(wu[i] @ x)
+        single.append(a * wd[i])
+        one = np.zeros(F, np.uint8)
+        one[i] = 1
+        np.testing.assert_allclose(oracle.ffn_masked(L, x, one), a * wd[i], rtol=1e-13,
+                                   atol=1e-15)
+    single = np.array(single)
+    for bits in range(1 << F):
+        m = np.array([(bits >> i) & 1 for i in range(F)], np.uint8)
+        y = oracle.ffn_masked(L, x, m)
+        np.testing.assert_allclose(y, single[m == 1].sum(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_all_active_relu_is_affine_map():
+    """With every pre-activation positive the ReLU FFN is the affine map
+    W_down (W_up x + b) -- a plain matrix product."""
+    rng = np.random.default_rng(9)
+    d, F = 12, 33
+    L = _rand_layer(rng, "relu", d, F)
+    L["b_act"] = np.full(F, 100.0, np.float32)
+    x = rng.standard_normal(d)
+    y, _ = oracle.ffn_dense(L, x)
+    ref = L["w_down_t"].astype(np.float64).T @ (L["w_up"].astype(np.float64) @ x + 100.0)
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+
+
+def test_all_active_reglu_is_quadratic_form():
+    """With every gate pre-activation positive the ReGLU FFN is
+    W_down ((W_gate x + b) * (W_up x))."""
+    rng = np.random.default_rng(10)
+    d, F = 12, 33
+    L = _rand_layer(rng, "reglu", d, F)
+    L["b_act"] = np.full(F, 100.0, np.float32)
+    x = rng.standard_normal(d)
+    y, _ = oracle.ffn_dense(L, x)
+    g = L["w_gate"].astype(np.float64) @ x + 100.0
+    u = L["w_up"].astype(np.float64) @ x
+    ref = L["w_down_t"].astype(np.float64).T @ (g * u)
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+
+
+def test_homogeneity_without_bias():
+    """Without bias, ReLU FFN is positively homogeneous of degree 1 and ReGLU of
+    degree 2 (powers of two keep it exact)."""
+    rng = np.random.default_rng(11)
+    for kind, deg in (("relu", 1), ("reglu", 2)):
+        L = _rand_layer(rng, kind, 16, 40)
+        L["b_act"] = None
+        x = rng.standard_normal(16)
+        y1 = oracle.ffn_dense(L, x)[0]
+        y4 = oracle.ffn_dense(L, 4.0 * x)[0]
+        assert np.array_equal(y4, (4.0 ** deg) * y1)
+
+
+def test_empty_mask_gives_zero():
+    rng = np.random.default_rng(12)
+    L = _rand_layer(rng, "reglu", 8, 20)
+    y = oracle.ffn_masked(L, rng.standard_normal(8), np.zeros(20, np.uint8))
+    assert np.all(y == 0.0)
+
+
+def test_sparse_rejects_bad_index():
+    rng = np.random.default_rng(13)
+    L = _rand_layer(rng, "relu", 8, 20)
+    with pytest.raises(ValueError):
+        oracle.ffn_sparse(L, np.zeros(8), np.array([3, 20], np.int32))
+
+
+def test_q4_0_ffn_matches_values():
+    """A 4-bit layer gives the same FFN as the fp32 layer holding its exact
+    dequantised values (which are exactly representable in fp32)."""
+    rng = np.random.default_rng(14)
+    d, F = 64, 24
+
+    def q4():
+        blocks = np.zeros((F, d // 32, 18), np.uint8)
+        s = np.abs(rng.standard_normal((F, d // 32)) * 0.05).astype(np.float16)
+        blocks[:, :, 0:2] = s.view(np.uint8).reshape(F, d // 32, 2)
+        blocks[:, :, 2:] = rng.integers(0, 256, size=(F, d // 32, 16), dtype=np.uint8)
+        return blocks.reshape(F, -1)
+    Lq = dict(kind="relu", w_dtype="q4_0", d=d, d_ffn=F, w_gate=None, w_up=q4(),
+              w_down_t=q4(), b_act=rng.standard_normal(F).astype(np.float32) * 0.1)
+    Lf = dict(Lq, w_dtype="f32", w_up=oracle.deq(Lq["w_up"], "q4_0", d).astype(np.float32),
+              w_down_t=oracle.deq(Lq["w_down_t"], "q4_0", d).astype(np.float32))
+    x = rng.standard_normal(d)
+    assert np.array_equal(oracle.ffn_dense(Lq, x)[0], oracle.ffn_dense(Lf, x)[0])
+
+
+# --------------------------------------------------------------------------- #
+# rms norm and decode glue
+# --------------------------------------------------------------------------- #
+def test_rmsnorm_closed_forms():
+    d = 64
+    c = 3.0
+    n = oracle.rmsnorm(np.full(d, c), 1e-5)
+    np.testing.assert_allclose(n, np.full(d, c / math.sqrt(c * c + 1e-5)), rtol=1e-15)
+    assert np.all(oracle.rmsnorm(np.zeros(d), 1e-5) == 0)
+    x = np.array([3.0, 4.0])  # mean square 12.5
+    np.testing.assert_allclose(oracle.rmsnorm(x, 0.0), x / math.sqrt(12.5), rtol=1e-15)
+
+
+def test_decode_zero_down_leaves_h_unchanged():
+    rng = np.random.default_rng(15)
+    L = _rand_layer(rng, "reglu", 16, 30)
+    L["w_down_t"] = np.zeros_like(L["w_down_t"])
+    h = rng.standard_normal((3, 16))
+    out = oracle.decode_layer(L, h, 1e-5)
+    assert np.array_equal(out["h"], h)
+
+
+def test_decode_layer_batch_union():
+    """Every token of a batch is computed on the union of the batch's masks."""
+    rng = np.random.default_rng(16)
+    L = _rand_layer(rng, "relu", 16, 40, r=8)
+    h = rng.standard_normal((4, 16)) * 2.0
+    out = oracle.decode_layer(L, h, 1e-5)
+    assert np.array_equal(out["union"], out["masks"].any(axis=0).astype(np.uint8))
+    for b in range(4):
+        n = oracle.rmsnorm(h[b], 1e-5)
+        assert np.array_equal(out["n"][b], n)
+        assert np.array_equal(out["y"][b], oracle.ffn_masked(L, n, out["union"]))
+
+
+# --------------------------------------------------------------------------- #
+# profile and hot-first permutation
+# --------------------------------------------------------------------------- #
+def test_profile_counts_brute_force():
+    rng = np.random.default_rng(17)
+    L = _rand_layer(rng, "reglu", 10, 25)
+    X = rng.standard_normal((30, 10))
+    counts = oracle.profile(L, X)
+    brute = np.zeros(25, np.int64)
+    for x in X:
+        brute += oracle.preact(L, x)[2]
+    assert np.array_equal(counts, brute)
+
+
+def test_hot_first_perm_properties():
+    rng = np.random.default_rng(18)
+    counts = rng.integers(0, 6, size=500)
+    perm = oracle.hot_first_perm(counts)
+    assert np.array_equal(np.sort(perm), np.arange(500))
+    c = counts[perm]
+    assert np.all(np.diff(c) <= 0)
+    for v in np.unique(counts):  # ties keep ascending original index
+        assert np.all(np.diff(perm[c == v]) > 0)
+    assert np.array_equal(perm, np.lexsort((np.arange(500), -counts)))
+
+
+def test_permuted_layer_same_output():
+    rng = np.random.default_rng(19)
+    L = _rand_layer(rng, "reglu", 16, 40, r=8)
+    X = rng.standard_normal((20, 16))
+    perm = oracle.hot_first_perm(oracle.profile(L, X))
+    P = oracle.permute_layer(L, perm)
+    for x in X[:5]:
+        y0 = oracle.ffn_dense(L, x)[0]
+        y1 = oracle.ffn_dense(P, x)[0]
+        np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-14)
+        m0 = oracle.predict(L, x)[2]
+        m1 = oracle.predict(P, x)[2]
+        assert np.array_equal(m1, m0[perm])
+        # stored indices map back through perm to the original active neurons
+        assert np.array_equal(np.sort(perm[oracle.compact(m1)]), oracle.compact(m0))
+
+
+def test_prototype_harness_structure():
+    """The Guide's Step 4 harness: budget 0.2 of 8192 neurons is 1638 hot; its
+    hand-built mask holds 400 + 50 = 450 neurons (5.49%); hot share of its
+    synthetic activations is about 0.774."""
+    g = load_golden("prototype_harness.json")
+    F = g["intermediate_size"]
+    rng = np.random.default_rng(20)
+    acts = np.zeros((g["profiled_tokens"], F), np.uint8)
+    acts[:, :g["hot_block"]] = rng.random((g["profiled_tokens"], g["hot_block"])) > 1 - g["p_hot"]
+    acts[:, g["hot_block"]:] = rng.random((g["profiled_tokens"], F - g["hot_block"])) > \
+        1 - g["p_cold"]
+    counts = acts.sum(axis=0)
+    k_hot, share = oracle.hot_share(counts, g["gpu_budget_ratio"])
+    assert k_hot == g["k_hot"]
+    assert abs(share - g["expected_hot_share_approx"]) < g["hot_share_tolerance"]
+    perm = oracle.hot_first_perm(counts)
+    hot, cold = perm[:k_hot], perm[k_hot:]
+    mask = np.zeros(F, np.uint8)
+    mask[hot[:g["mask_hot"]]] = 1
+    mask[cold[:g["mask_cold"]]] = 1
+    idx = oracle.compact(mask)
+    assert idx.size == g["mask_active"]
+    assert round(100.0 * idx.size / F, 2) == g["mask_active_percent_2dp"]

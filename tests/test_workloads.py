@@ -1,0 +1,97 @@
+"""The synthetic-workload generator: firing statistics, reproducibility and the
+4-bit block packing.  CPU only (tiny shapes)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import (ALL, TINY, firing_probs, layer_to_numpy, make_layer, make_tokens,
+                       q4_0_pack, q4_0_values)
+
+
+@pytest.mark.parametrize("name", list(ALL))
+def test_firing_probs(name):
+    c = ALL[name]
+    p = firing_probs(c.d_ffn, c.gamma, c.mean_activity)
+    assert abs(p.mean() - c.mean_activity) < 1e-12
+    assert np.all(np.diff(p) <= 0) and p.max() < 1.0 and p.min() > 0.0
+    # unsaturated ranks follow k^-gamma exactly
+    k = np.arange(1, c.d_ffn + 1)
+    free = p < p.max()
+    slope = np.polyfit(np.log(k[free]), np.log(p[free]), 1)[0]
+    assert abs(slope + c.gamma) < 1e-9
+
+
+@pytest.fixture(scope="module")
+def tiny_layer():
+    return layer_to_numpy(make_layer(TINY, 0, seed=0))
+
+
+def test_realised_activity(tiny_layer):
+    """Exact-mask firing on fresh N(0, I) tokens matches the target p_i."""
+    L = tiny_layer
+    N = 800
+    X = make_tokens(TINY.d, N, 1, seed=5).numpy()[:, 0, :]
+    counts = oracle.profile(L, X)
+    rate = counts / N
+    p = L["p_fire"]
+    # aggregate activity within 4 sigma of the binomial mean
+    sigma = math.sqrt((p * (1 - p)).sum() * N)
+    assert abs(counts.sum() - p.sum() * N) < 4 * sigma
+    # per neuron: |rate - p| within 4.5 sigma for almost every neuron
+    s = np.sqrt(p * (1 - p) / N)
+    assert np.mean(np.abs(rate - p) <= 4.5 * s + 1.0 / N) > 0.99
+    # realised hot-first ordering recovers the planted power law roughly
+    perm = oracle.hot_first_perm(counts)
+    top = int(0.2 * L["d_ffn"])
+    share = counts[perm[:top]].sum() / counts.sum()
+    assert 0.65 < share < 0.85
+
+
+def test_predictor_density(tiny_layer):
+    """The fitted predictor marks about the configured share of neurons active
+    and agrees with the exact mask far better than chance."""
+    L = dict(tiny_layer, t=oracle.logit_threshold(TINY.tau))
+    X = make_tokens(TINY.d, 64, 1, seed=6).numpy()[:, 0, :]
+    dens, rec = [], []
+    for x in X:
+        m = oracle.predict(L, x)[2]
+        em = oracle.preact(L, x)[2]
+        dens.append(m.mean())
+        rec.append((m & em).sum() / max(1, em.sum()))
+    assert abs(np.mean(dens) - TINY.mean_activity) < 0.02
+    assert np.mean(rec) > 3 * TINY.mean_activity
+
+
+def test_seed_reproducible():
+    a = make_layer(TINY, 1, seed=3)
+    b = make_layer(TINY, 1, seed=3)
+    c = make_layer(TINY, 1, seed=4)
+    for k in ("w_up", "w_down_t", "b_act", "p_w1", "p_w2", "p_b2"):
+        assert torch.equal(a[k], b[k])
+        assert not torch.equal(a[k], c[k])
+    assert torch.equal(make_tokens(64, 3, 2, seed=1), make_tokens(64, 3, 2, seed=1))
+
+
+def test_q4_0_pack_layout():
+    """Packed blocks read back through the oracle's block reader give exactly
+    (code - 8) * scale."""
+    g = torch.Generator().manual_seed(0)
+    rows, cols = 5, 96
+    codes = torch.randint(0, 16, (rows, cols), generator=g, dtype=torch.uint8)
+    scales = (torch.randn(rows, cols // 32, generator=g) * 0.01).abs().half()
+    packed = q4_0_pack(codes, scales).numpy()
+    assert packed.shape == (rows, cols // 32 * 18)
+    vals = oracle.deq(packed, "q4_0", cols)
+    assert np.array_equal(vals, q4_0_values(codes, scales).double().numpy())
+
+
+def test_q4_0_layer_generation():
+    from dataclasses import replace
+    cfg = replace(ALL["opt_175b_relu_q4_0"], d=128, d_ffn=256, r=32, layers=1)
+    L = make_layer(cfg, 0, seed=0, n_cal=512, return_values=True)
+    assert L["w_up"].dtype == torch.uint8 and L["w_up"].shape == (256, 128 // 32 * 18)
+    vals = oracle.deq(L["w_up"].numpy(), "q4_0", 128)
+    assert np.array_equal(vals, L["act_values"].double().numpy())

@@ -1,0 +1,62 @@
+"""The five synthetic FFN-stack workloads (shapes of real model families).
+
+Each entry fixes the FFN shape, the weight storage, the power-law firing
+statistics and the predictor size.  Firing follows [Guide] section 1: the
+activation frequency of the rank-k neuron falls off as k^-gamma, gamma > 1
+("PowerInfer Guide: Exploiting Activation Sparsity for LLM AI", section 1
+"Empirical Power-Law Distribution and Skewness").  Mean activities of 5-10%
+sit in that page's "80% to 90% of neurons are exactly zero" band
+("The Hidden Inefficiency").
+"""
+from dataclasses import dataclass, field
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    kind: str            # "relu" (non-gated up/down) or "reglu" (gated)
+    d: int
+    d_ffn: int
+    layers: int
+    w_dtype: str         # "f32" | "f16" | "q4_0"
+    p_dtype: str         # predictor weights: "f32" | "f16"
+    r: int               # predictor hidden width
+    gamma: float         # power-law exponent of firing probability vs rank
+    mean_activity: float
+    tokens: int
+    batches: Tuple[int, ...] = (1,)
+    w_std: float = 0.02  # std of fp weights (fp32 / fp16 configs)
+    q4_scale_std: float = 0.003  # std of the |N(0, s^2)| block scales (q4_0)
+    tau: float = 0.5
+    hot_first: bool = False
+    description: str = field(default="", compare=False)
+
+
+TINY = Config(
+    name="tiny_relu", kind="relu", d=256, d_ffn=1024, layers=2, w_dtype="f32", p_dtype="f32",
+    r=64, gamma=1.2, mean_activity=0.10, tokens=16, w_std=256 ** -0.5,
+    description="Tiny ReLU FFN (OPT-style, non-gated), fp32 weights ~N(0, 1/d)")
+
+LLAMA2_7B = Config(
+    name="llama2_7b_reglu", kind="reglu", d=4096, d_ffn=11008, layers=32, w_dtype="f16",
+    p_dtype="f16", r=1024, gamma=1.2, mean_activity=0.10, tokens=128,
+    description="Llama2-7B-shaped ReGLU FFN (ProSparse-like), fp16")
+
+FALCON_40B = Config(
+    name="falcon_40b_relu", kind="relu", d=8192, d_ffn=32768, layers=60, w_dtype="f16",
+    p_dtype="f16", r=1024, gamma=1.1, mean_activity=0.08, tokens=128, batches=(1, 8),
+    description="Falcon-40B-shaped ReLU FFN (non-gated up/down), fp16")
+
+LLAMA2_70B = Config(
+    name="llama2_70b_reglu", kind="reglu", d=8192, d_ffn=28672, layers=80, w_dtype="f16",
+    p_dtype="f16", r=1024, gamma=1.2, mean_activity=0.10, tokens=256, batches=(1, 4, 16),
+    hot_first=True,
+    description="Llama2-70B-shaped ReGLU FFN, fp16, hot-first permuted rows")
+
+OPT_175B_Q4 = Config(
+    name="opt_175b_relu_q4_0", kind="relu", d=12288, d_ffn=49152, layers=96, w_dtype="q4_0",
+    p_dtype="f16", r=1024, gamma=1.3, mean_activity=0.05, tokens=128,
+    description="OPT-175B-shaped ReLU FFN with 4-bit (Q4_0 block) weights, fp16 predictor")
+
+ALL = {c.name: c for c in (TINY, LLAMA2_7B, FALCON_40B, LLAMA2_70B, OPT_175B_Q4)}

@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the neuron-sparse FFN: weights, biases, predictor
+parameters and tokens.
+
+This module only *constructs* inputs; both the CPU oracle and the GPU path
+consume what it returns, and neither imports the other.  Everything is drawn
+from torch generators seeded by (seed, layer, tensor tag), so a given call
+reproduces bit-identical tensors on a given device type.
+
+Construction (one layer):
+  * firing probability of the rank-k neuron p_k = min(1 - 1e-6, c * k^-gamma),
+    c chosen by bisection so that mean(p) equals the configured activity
+    ([Guide] section 1 power law P(k) ~ k^-gamma); ranks are dealt to neurons
+    by a seeded random permutation, so the stored order is not hot-first;
+  * fp weights ~ N(0, std^2), rounded to the storage type; 4-bit weights are
+    blocks of 32 codes uniform on 0..15 with an fp16 scale |N(0, s^2)|;
+  * bias of the activated projection b_i = ||w_i|| * Phi^-1(p_i), so that
+    P(w_i . x + b_i > 0) = p_i for x ~ N(0, I);
+  * predictor: W1 ~ N(0, 1/d), b1 = 0; [W2 | b2] by ridge least squares of
+    the true pre-activations on the hidden features over calibration tokens,
+    then b2_i shifted so that the calibration firing rate of neuron i is p_i.
+"""
+import math
+
+import numpy as np
+import torch
+
+from .configs import Config
+
+# tensor tags mixed into the per-tensor seed
+TAG_RANK, TAG_GATE, TAG_UP, TAG_DOWN, TAG_W1, TAG_CAL = 1, 2, 3, 4, 5, 6
+TAG_Q4_CODES, TAG_Q4_SCALES = 7, 8
+TAG_TOKENS, TAG_PROFILE = 20, 21
+
+Q4_0_BLOCK, Q4_0_BYTES = 32, 18
+
+
+def _gen(device, seed, layer, tag):
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + (layer + 1) * 10_007 + tag * 101) % (2 ** 63 - 1))
+    return g
+
+
+def firing_probs(d_ffn, gamma, mean, cap=1.0 - 1e-6):
+    """p_k for ranks k = 1..d_ffn (descending), mean(p) == mean."""
+    k = np.arange(1, d_ffn + 1, dtype=np.float64)
+    base = k ** -gamma
+    lo, hi = 0.0, 1.0
+    while np.minimum(cap, hi * base).mean() < mean:
+        hi *= 2.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if np.minimum(cap, mid * base).mean() < mean:
+            lo = mid
+        else:
+            hi = mid
+    return np.minimum(cap, hi * base)
+
+
+def q4_0_pack(codes, scales):
+    """codes uint8 [rows, cols] in 0..15, scales fp16 [rows, cols/32] -> uint8
+    [rows, cols/32*18] blocks: 2 scale bytes (little-endian), then 16 bytes whose
+    byte k holds code k (low nibble) and code k+16 (high nibble)."""
+    rows, cols = codes.shape
+    nb = cols // Q4_0_BLOCK
+    c = codes.reshape(rows, nb, Q4_0_BLOCK).to(torch.int32)
+    packed = (c[:, :, :16] | (c[:, :, 16:] << 4)).to(torch.uint8)
+    sb = scales.contiguous().view(torch.int16).to(torch.int32) & 0xFFFF
+    lo = (sb & 0xFF).to(torch.uint8).unsqueeze(-1)
+    hi = (sb >> 8).to(torch.uint8).unsqueeze(-1)
+    return torch.cat([lo, hi, packed], dim=-1).reshape(rows, nb * Q4_0_BYTES).contiguous()
+
+
+def q4_0_values(codes, scales):
+    """Exact fp32 values (code - 8) * scale of unpacked 4-bit weights."""
+    rows, cols = codes.shape
+    s = scales.float().repeat_interleave(Q4_0_BLOCK, dim=1)
+    return (codes.float() - 8.0) * s
+
+
+def _weights(cfg, g_codes_or_normal, g_scales, shape, device):
+    """(stored tensor, fp32 values) of one weight matrix."""
+    rows, cols = shape
+    if cfg.w_dtype == "q4_0":
+        codes = torch.randint(0, 16, shape, generator=g_codes_or_normal, device=device,
+                              dtype=torch.uint8)
+        scales = (torch.randn(rows, cols // Q4_0_BLOCK, generator=g_scales, device=device)
+                  * cfg.q4_scale_std).abs().half()
+        vals = q4_0_values(codes, scales)
+        return q4_0_pack(codes, scales), vals
+    w = torch.randn(shape, generator=g_codes_or_normal, device=device) * cfg.w_std
+    if cfg.w_dtype == "f16":
+        w = w.half()
+        return w, w.float()
+    return w, w
+
+
+def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int = 4096,
+               return_values: bool = False):
+    """One layer of `cfg` as a dict of torch tensors on `device`.
+
+    Keys: kind, w_dtype, p_dtype, d, d_ffn, r, tau, w_gate (ReGLU) / None,
+    w_up, w_down_t ([d_ffn, d], W_down transposed), b_act fp32 [d_ffn],
+    p_w1 [r, d], p_b1 fp32 [r], p_w2 [d_ffn, r], p_b2 fp32 [d_ffn],
+    p_fire float64 numpy [d_ffn] (target firing probability per neuron)."""
+    dev = torch.device(device)
+    d, F, r = cfg.d, cfg.d_ffn, cfg.r
+    if cfg.w_dtype == "q4_0" and d % Q4_0_BLOCK:
+        raise ValueError("4-bit blocks need d % 32 == 0")
+
+    p_rank = firing_probs(F, cfg.gamma, cfg.mean_activity)
+    order = torch.randperm(F, generator=_gen(dev, seed, layer, TAG_RANK), device=dev).cpu()
+    p = p_rank[order.numpy()]
+
+    def w(tag):
+        return _weights(cfg, _gen(dev, seed, layer, tag), _gen(dev, seed, layer, tag + 40),
+                        (F, d), dev)
+
+    if cfg.kind == "reglu":
+        w_gate, act_vals = w(TAG_GATE)
+        w_up, _ = w(TAG_UP)
+    else:
+        w_gate = None
+        w_up, act_vals = w(TAG_UP)
+    w_down_t, _ = w(TAG_DOWN)
+
+    norms = act_vals.double().norm(dim=1)
+    b_act = (norms * torch.special.ndtri(torch.from_numpy(p).to(dev))).float()
+
+    # predictor first layer
+    w1 = torch.randn(r, d, generator=_gen(dev, seed, layer, TAG_W1), device=dev) * d ** -0.5
+    if cfg.p_dtype == "f16":
+        w1 = w1.half()
+    b1 = torch.zeros(r, device=dev)
+
+    # second layer fitted on calibration tokens
+    xc = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_CAL), device=dev)
+    hcal = torch.relu(xc @ w1.float().t() + b1)
+    zcal = xc @ act_vals.t() + b_act
+    del xc
+    ha = torch.cat([hcal, torch.ones(n_cal, 1, device=dev)], dim=1).double()
+    A = ha.t() @ ha
+    lam = 1e-3 * float(torch.trace(A[:r, :r])) / r
+    A[:r, :r] += lam * torch.eye(r, device=dev, dtype=torch.float64)
+    Ainv = torch.from_numpy(np.linalg.inv(A.cpu().numpy())).to(dev)
+    sol = Ainv @ (ha.t() @ zcal.double())          # [r+1, F]
+    del zcal
+    w2 = sol[:r].t().float().contiguous()
+    b2 = sol[r].float()
+    if cfg.p_dtype == "f16":
+        w2 = w2.half()
+    lcal = hcal @ w2.float().t() + b2                # [n_cal, F]
+    srt = torch.sort(lcal, dim=0, descending=True).values
+    del lcal
+    k = torch.from_numpy(np.clip(np.rint(p * n_cal), 0, n_cal).astype(np.int64)).to(dev)
+    cols = torch.arange(F, device=dev)
+    top = srt[0]
+    upper = srt[(k - 1).clamp(min=0), cols]
+    lower = srt[k.clamp(max=n_cal - 1), cols]
+    q = torch.where(k == 0, top, torch.where(k == n_cal, srt[n_cal - 1] - 1.0,
+                                                0.5 * (upper + lower)))
+    b2 = (b2 - q).float()
+    del srt
+
+    out = dict(kind=cfg.kind, w_dtype=cfg.w_dtype, p_dtype=cfg.p_dtype, d=d, d_ffn=F, r=r,
+               tau=cfg.tau, w_gate=w_gate, w_up=w_up, w_down_t=w_down_t,
+               b_act=b_act.contiguous(), p_w1=w1.contiguous(), p_b1=b1.contiguous(),
+               p_w2=w2.contiguous(), p_b2=b2.contiguous(), p_fire=p)
+    if return_values:
+        out["act_values"] = act_vals
+    return out
+
+
+def make_tokens(d: int, T: int, B: int, seed: int = 0, device="cpu", tag: int = TAG_TOKENS):
+    """Decode inputs x ~ N(0, I): [T, B, d] fp32 (one fresh batch per step)."""
+    dev = torch.device(device)
+    return torch.randn(T, B, d, generator=_gen(dev, seed, -1, tag), device=dev)
+
+
+def make_profile_tokens(d: int, N: int, seed: int = 0, device="cpu"):
+    """Calibration tokens for the hot-first activation profile: [N, d] fp32."""
+    return make_tokens(d, N, 1, seed, device, tag=TAG_PROFILE)[:, 0, :].contiguous()
+
+
+def layer_to_numpy(layer):
+    """The layer dict with every tensor moved to host numpy (for the oracle)."""
+    out = {}
+    for k, v in layer.items():
+        if isinstance(v, torch.Tensor):
+            out[k] = v.detach().cpu().numpy()
+        else:
+            out[k] = v
+    return out
