@@ -1,0 +1,202 @@
+// Device helpers for the row-streaming kernels of libspffn (gfx950, wave64).
+//
+// Every weight row is read as 16-byte "packets", one per lane per step, so a
+// wave moves 1 KiB of weights per load instruction (128-bit loads, fully
+// coalesced).  A packet is 4 fp32, 8 fp16, or one 4-bit block of 32 codes.
+//
+// Activations are staged in LDS in a packet-transposed layout so that lane p
+// reads the values for its packet as float4s at consecutive addresses (no bank
+// conflicts):  for a chunk of NP packets of E elements,
+//     xl[b * NP*E + (g * NP + p) * 4 + n] = x[b][c0 + p*E + 4*g + n]
+// with g < E/4, n < 4.  For 4-bit packets the per-block sums of x are kept too
+// (xsum[b * NP + p]), so a block's dot product is  s * (sum q_k x_k - 8 sum x_k).
+#pragma once
+
+#include "internal.h"
+
+namespace spffn {
+
+template <int FMT> struct PacketElems;
+template <> struct PacketElems<kF32> { static constexpr int value = 4; };
+template <> struct PacketElems<kF16> { static constexpr int value = 8; };
+template <> struct PacketElems<kQ4> { static constexpr int value = 32; };
+
+inline int packet_elems(int fmt) { return fmt == kF32 ? 4 : fmt == kF16 ? 8 : 32; }
+
+// Bytes of one stored row of `cols` elements.
+template <int FMT>
+__host__ __device__ __forceinline__ size_t row_bytes(int cols) {
+    return FMT == kF32 ? (size_t)cols * 4 : FMT == kF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+}
+
+template <int FMT>
+__device__ __forceinline__ const uint4 *row_ptr(const WMat &w, size_t row, int cols) {
+    return reinterpret_cast<const uint4 *>(w.data + row * row_bytes<FMT>(cols));
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+template <int FMT>
+__device__ __forceinline__ float packet_scale(const WMat &w, size_t row, int cols, int pg) {
+    if constexpr (FMT == kQ4)
+        return half_bits_to_float(w.scales[row * (size_t)(cols / 32) + pg]);
+    else
+        return 1.0f;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Stage tokens x[b][c0 .. c0 + NP*E) for b < NB (zeros for b >= B) into LDS.
+// Call between barriers; when `xsum` is given, a second barrier-separated
+// pass (stage_xsum) fills the 4-bit block sums.
+template <int E, int NB>
+__device__ __forceinline__ void stage_x(const float *__restrict__ x, int B, int ld, int c0, int NP,
+                                        float *xl) {
+    const int ncols = NP * E;
+    for (int t = threadIdx.x; t < NB * ncols; t += blockDim.x) {
+        const int b = t / ncols, c = t - b * ncols;
+        const float v = (b < B) ? x[(size_t)b * ld + c0 + c] : 0.0f;
+        const int p = c / E, k = c - p * E;
+        xl[b * ncols + ((k >> 2) * NP + p) * 4 + (k & 3)] = v;
+    }
+}
+
+template <int E, int NB>
+__device__ __forceinline__ void stage_xsum(const float *xl, int NP, float *xsum) {
+    const int ncols = NP * E;
+    for (int t = threadIdx.x; t < NB * NP; t += blockDim.x) {
+        const int b = t / NP, p = t - b * NP;
+        const float *base = xl + b * ncols;
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < E / 4; ++g) {
+            const float4 v = *reinterpret_cast<const float4 *>(base + (g * NP + p) * 4);
+            s += v.x;
+            s += v.y;
+            s += v.z;
+            s += v.w;
+        }
+        xsum[t] = s;
+    }
+}
+
+__device__ __forceinline__ float4 lds4(const float *xl, int NP, int g, int p) {
+    return *reinterpret_cast<const float4 *>(xl + (g * NP + p) * 4);
+}
+
+// acc[b] += dot(packet, x_b restricted to the packet's columns).
+template <int FMT, int NB>
+__device__ __forceinline__ void packet_dot(const uint4 raw, float scale, const float *xl, int NP,
+                                           int p, const float *xsum, float (&acc)[NB]) {
+    constexpr int E = PacketElems<FMT>::value;
+    const int XS = NP * E;
+    if constexpr (FMT == kF32) {
+        const float w0 = __uint_as_float(raw.x), w1 = __uint_as_float(raw.y);
+        const float w2 = __uint_as_float(raw.z), w3 = __uint_as_float(raw.w);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float4 v = lds4(xl + b * XS, NP, 0, p);
+            float a = acc[b];
+            a = fmaf(w0, v.x, a);
+            a = fmaf(w1, v.y, a);
+            a = fmaf(w2, v.z, a);
+            a = fmaf(w3, v.w, a);
+            acc[b] = a;
+        }
+    } else if constexpr (FMT == kF16) {
+        typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+        const half8 h = __builtin_bit_cast(half8, raw);
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (float)h[e];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float4 v0 = lds4(xl + b * XS, NP, 0, p);
+            const float4 v1 = lds4(xl + b * XS, NP, 1, p);
+            float a = acc[b];
+            a = fmaf(w[0], v0.x, a);
+            a = fmaf(w[1], v0.y, a);
+            a = fmaf(w[2], v0.z, a);
+            a = fmaf(w[3], v0.w, a);
+            a = fmaf(w[4], v1.x, a);
+            a = fmaf(w[5], v1.y, a);
+            a = fmaf(w[6], v1.z, a);
+            a = fmaf(w[7], v1.w, a);
+            acc[b] = a;
+        }
+    } else {
+        // 4-bit block: word m holds codes 4m..4m+3 in its low nibbles (group m)
+        // and codes 16+4m..16+4m+3 in its high nibbles (group 4+m).
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        float q[32];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
+            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                q[4 * m + n] = (float)((lo >> (8 * n)) & 0xFFu);
+                q[16 + 4 * m + n] = (float)((hi >> (8 * n)) & 0xFFu);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float sq = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const float4 v = lds4(xl + b * XS, NP, g, p);
+                sq = fmaf(q[4 * g + 0], v.x, sq);
+                sq = fmaf(q[4 * g + 1], v.y, sq);
+                sq = fmaf(q[4 * g + 2], v.z, sq);
+                sq = fmaf(q[4 * g + 3], v.w, sq);
+            }
+            acc[b] = fmaf(scale, fmaf(-8.0f, xsum[b * NP + p], sq), acc[b]);
+        }
+    }
+}
+
+// Unpack one packet into E fp32 weights (used by the down projection, which
+// scales whole rows rather than dotting them).
+template <int FMT>
+__device__ __forceinline__ void packet_values(const uint4 raw, float scale,
+                                              float (&w)[PacketElems<FMT>::value]) {
+    if constexpr (FMT == kF32) {
+        w[0] = __uint_as_float(raw.x);
+        w[1] = __uint_as_float(raw.y);
+        w[2] = __uint_as_float(raw.z);
+        w[3] = __uint_as_float(raw.w);
+    } else if constexpr (FMT == kF16) {
+        typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+        const half8 h = __builtin_bit_cast(half8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (float)h[e];
+    } else {
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
+            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                w[4 * m + n] = ((float)((lo >> (8 * n)) & 0xFFu) - 8.0f) * scale;
+                w[16 + 4 * m + n] = ((float)((hi >> (8 * n)) & 0xFFu) - 8.0f) * scale;
+            }
+        }
+    }
+}
+
+// Column of packet element e within its row: packets hold consecutive columns,
+// except 4-bit blocks, whose element order is already the column order
+// (code k is column k of the block).
+template <int FMT>
+__device__ __forceinline__ int packet_col(int p, int e) {
+    return p * PacketElems<FMT>::value + e;
+}
+
+}  // namespace spffn

@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP sources of libspffn (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spffn.h"
+
+namespace spffn {
+
+constexpr int kWave = 64;
+
+// Weight storage formats.  A "packet" is the 16 bytes one lane loads at a time:
+// 4 fp32, 8 fp16, or one 4-bit block of 32 codes (whose fp16 scale lives in a
+// separate array).
+enum Fmt : int { kF32 = 0, kF16 = 1, kQ4 = 2 };
+
+// One weight matrix [rows, cols] in device memory.
+struct WMat {
+    const uint8_t *data;     // fp32/fp16 elements, or the 4-bit code region
+    const uint16_t *scales;  // 4-bit only: fp16 scale bits [rows, cols/32]
+};
+
+// Host-side layer handle (the C ABI's opaque spffn_layer).
+struct Layer {
+    spffn_layer_desc desc;
+    float t;  // logit threshold ln(tau / (1 - tau)), binary64 rounded to binary32
+    WMat gate, up, down, w1, w2;
+};
+
+// Workspace carve-up for a batch of B tokens.
+struct WsLayout {
+    size_t n, hid, mask, uni, idx, count, act, part, total;
+    int chunks;  // neuron chunks of the down projection (partial-sum slots)
+};
+
+WsLayout layer_ws_layout(const Layer &L, int B);
+
+// ---- launchers (each returns hipSuccess or the launch error) ---------------
+hipError_t launch_threshold(const float *logits, int64_t n, float t, uint8_t *mask,
+                            hipStream_t s);
+hipError_t launch_compact(const uint8_t *mask, int n, int32_t *idx, int32_t *count,
+                          hipStream_t s);
+hipError_t launch_hot_first_order(const int32_t *counts, int n, int32_t *perm, hipStream_t s);
+hipError_t launch_permute_rows(const void *src, void *dst, const int32_t *perm, int rows,
+                               int64_t row_bytes, hipStream_t s);
+hipError_t launch_q4_0_repack(const void *aos, void *soa, int rows, int cols, hipStream_t s);
+
+// Dense row GEMVs of the predictor and the profile.
+//   hid[b, j]   = max(W1[j] . x_b + b1[j], 0)
+//   logits/mask = W2[i] . hid_b + b2[i] > t, union over b
+//   counts[i]  += #{b : W[i] . x_b + bias[i] > 0}
+hipError_t launch_gemv_hid(int fmt, WMat w, int rows, int cols, const float *x, int B,
+                           const float *bias, float *out, hipStream_t s);
+hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x, int B,
+                            const float *bias, float t, float *logits, uint8_t *mask,
+                            uint8_t *uni, hipStream_t s);
+hipError_t launch_gemv_count(int fmt, WMat w, int rows, int cols, const float *x, int B,
+                             const float *bias, int32_t *counts, hipStream_t s);
+
+// Gathered FFN.  idx == nullptr means every neuron (dense).
+hipError_t launch_ffn_up(const Layer &L, const float *x, int B, const int32_t *idx,
+                         const int32_t *count, float *act, hipStream_t s);
+hipError_t launch_ffn_down(const Layer &L, int B, const int32_t *idx, const int32_t *count,
+                           const float *act, float *part, int chunks, hipStream_t s);
+// y[b, k] = sum_c part[c, b, k] (+ resid[b, k] when resid != nullptr)
+hipError_t launch_reduce(const float *part, int chunks, int B, int d, const float *resid,
+                         float *y, hipStream_t s);
+hipError_t launch_rmsnorm(const float *h, int B, int d, float eps, float *n, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int32_t v, int n, hipStream_t s);
+hipError_t launch_copy_words(const void *src, void *dst, int64_t n_words, hipStream_t s);
+
+int down_chunks(const Layer &L);
+
+}  // namespace spffn

@@ -1,0 +1,250 @@
+/*
+ * spffn.h -- C ABI of the neuron-sparse FFN library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the library computes, per token and per FFN layer:
+ *   1. a two-layer MLP predictor scores every FFN neuron and a threshold turns
+ *      the scores into an active-neuron mask
+ *        ("PowerInfer_x64: Neuron-Level Sparse Inference Makes Large Models
+ *          Fly on Consumer GPUs", list item 2 "Prediction and Caching";
+ *         "PowerInfer Guide: Exploiting Activation Sparsity for LLM AI",
+ *          section 3 "Adaptive Online Neuron Predictors", predictor equation);
+ *   2. the mask is compacted into an ascending list of active neuron indices
+ *        (Guide, Step 3 "Fused PowerInfer Sparse FFN Module", and section 4
+ *         "Neuron-Aware Sparse GPU Operators": the bitmask is decoded and only
+ *         active indices are computed);
+ *   3. only the active rows of W_up (and W_gate) are read, activated with
+ *      ReLU (or ReLU(gate) * up), and only the matching columns of W_down are
+ *      accumulated into the output
+ *        (Guide, "The Hidden Inefficiency": FFN(x) = W_down (sigma(W_gate x)
+ *         (*) (W_up x)); Step 3 for the non-gated ReLU form).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked [host].  Every call only
+ *     enqueues work on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and returns; no call synchronises the host, and no call
+ *     allocates or frees device memory.  Outputs and workspaces belong to the
+ *     caller.  Weight pointers in a layer description are BORROWED: the caller
+ *     keeps them alive and unchanged while any handle that refers to them is
+ *     used.
+ *   - Activations (x, y, h, logits) are fp32.  Masks are uint8 0/1 (the byte
+ *     layout of a torch.bool tensor); any nonzero byte counts as set on input.
+ *     Neuron indices are int32 and refer to STORED rows (after any load-time
+ *     permutation).
+ *   - Matrices are row-major.  W_down is stored TRANSPOSED as W_down_t
+ *     [d_ffn, d], so neuron i's output column is one contiguous row.
+ *   - Errors: argument, shape, dtype and workspace checks return a negative
+ *     spffn_status before anything is enqueued; a failed kernel launch returns
+ *     SPFFN_E_HIP.  spffn_last_error() gives the text of the calling thread's
+ *     last failure.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.
+ *   - Calls that share a workspace must not overlap (use one stream per
+ *     workspace).
+ */
+#ifndef SPFFN_H
+#define SPFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPFFN_OK = 0,
+    SPFFN_E_ARG = -1,       /* null / misaligned pointer, bad enum, bad flag     */
+    SPFFN_E_SHAPE = -2,     /* a size out of range or not a multiple it must be  */
+    SPFFN_E_DTYPE = -3,     /* a storage type the call does not accept           */
+    SPFFN_E_WORKSPACE = -4, /* workspace missing or smaller than required        */
+    SPFFN_E_HIP = -5        /* a HIP runtime call or kernel launch failed        */
+} spffn_status;
+
+typedef enum {
+    SPFFN_F32 = 0,  /* IEEE binary32                                           */
+    SPFFN_F16 = 1,  /* IEEE binary16                                           */
+    SPFFN_Q4_0 = 2  /* 4-bit blocks of 32 codes with an fp16 scale; on the GPU
+                       in the split layout written by spffn_q4_0_repack       */
+} spffn_dtype;
+
+typedef enum {
+    SPFFN_RELU = 0,  /* non-gated: a_i = max(W_up[i] . x + b_i, 0)               */
+    SPFFN_REGLU = 1  /* gated:     a_i = max(W_gate[i] . x + b_i, 0) * (W_up[i] . x) */
+} spffn_kind;
+
+/* Maximum number of tokens per call (batch B). */
+#define SPFFN_MAX_BATCH 16
+
+/* [host] Description of one FFN layer and its predictor.
+ *   w_gate    [d_ffn, d]  ReGLU only (NULL for ReLU)
+ *   w_up      [d_ffn, d]
+ *   w_down_t  [d_ffn, d]  W_down transposed
+ *   b_act     fp32 [d_ffn] bias of the activated projection (gate for ReGLU,
+ *             up for ReLU), or NULL for none
+ *   p_w1 [r, d], p_b1 fp32 [r], p_w2 [d_ffn, r], p_b2 fp32 [d_ffn]
+ *   tau       probability threshold in (0, 1): neuron i is predicted active
+ *             when sigmoid(logit_i) > tau, evaluated as logit_i > t with
+ *             t = ln(tau / (1 - tau)) computed once in binary64 and rounded to
+ *             binary32 (sigmoid is increasing)
+ * FFN weights are w_dtype (F32, F16 or Q4_0 split layout); predictor weights
+ * are p_dtype (F32 or F16).  Shapes: F32 needs d % 4 == 0, F16 d % 8 == 0,
+ * Q4_0 d % 32 == 0; the predictor needs d and r multiples of 4 (F32) or 8
+ * (F16).  Every weight pointer must be 16-byte aligned. */
+typedef struct {
+    int32_t d, d_ffn, r;
+    int32_t kind;     /* spffn_kind  */
+    int32_t w_dtype;  /* spffn_dtype */
+    int32_t p_dtype;  /* spffn_dtype */
+    float tau;
+    int32_t reserved; /* must be 0 */
+    const void *w_gate;
+    const void *w_up;
+    const void *w_down_t;
+    const float *b_act;
+    const void *p_w1;
+    const float *p_b1;
+    const void *p_w2;
+    const float *p_b2;
+} spffn_layer_desc;
+
+typedef struct spffn_layer spffn_layer; /* [host] opaque, immutable after create */
+typedef struct spffn_model spffn_model; /* [host] opaque: an ordered layer stack  */
+
+/* [host] Optional per-layer record of a decode step, for tests.  Any member
+ * may be NULL.  h_in [L, B, d]: the residual stream entering each layer;
+ * union_mask [sum_l d_ffn_l]: each layer's union mask, layers concatenated;
+ * logits [sum_l B * d_ffn_l]: each layer's predictor logits [B, d_ffn_l]. */
+typedef struct {
+    float *h_in;
+    uint8_t *union_mask;
+    float *logits;
+} spffn_trace;
+
+/* ---- handles --------------------------------------------------------- */
+
+/* Validate `desc` and build a layer handle (a small host struct; the weights
+ * stay borrowed).  *out is set only on SPFFN_OK. */
+spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out);
+void spffn_layer_destroy(spffn_layer *layer);
+
+/* [host] The binary32 logit threshold t the layer compares against (NaN for
+ * a NULL layer). */
+float spffn_layer_threshold(const spffn_layer *layer);
+
+/* An ordered stack of layers sharing one model width d.  `layers` is a host
+ * array of L handles, which stay owned by the caller and must outlive the
+ * model.  rms_eps is the epsilon of the gainless RMS normalisation applied to
+ * the residual stream before every layer. */
+spffn_status spffn_model_create(const spffn_layer *const *layers, int32_t n_layers,
+                                float rms_eps, spffn_model **out);
+void spffn_model_destroy(spffn_model *model);
+
+/* Bytes of device workspace that spffn_predict / spffn_forward (layer) and
+ * spffn_decode_step (model) need for a batch of B tokens; 0 on bad input.
+ * The workspace must be 256-byte aligned. */
+size_t spffn_layer_workspace_bytes(const spffn_layer *layer, int32_t B);
+size_t spffn_model_workspace_bytes(const spffn_model *model, int32_t B);
+
+/* ---- the hot path ----------------------------------------------------- */
+
+/* Threshold given logits: mask[i] = logits[i] > t for i < n (strict; NaN is
+ * inactive).  Guide section 3 threshold; sigmoid replaced by its logit, as in
+ * spffn_layer_desc. */
+spffn_status spffn_threshold(const float *logits, int64_t n, float t, uint8_t *mask,
+                             void *stream);
+
+/* Compaction: idx[0 .. count) = the i < n with mask[i] != 0, ascending;
+ * *count (device int32) = their number.  idx must hold n entries; entries at
+ * and after count are left unspecified.  1 <= n < 2^31; mask 16-byte aligned
+ * is fastest but not required.  Guide Step 3 (the active positions of the
+ * mask) and section 4 (the activation bitmask decoded into indices). */
+spffn_status spffn_compact(const uint8_t *mask, int32_t n, int32_t *idx, int32_t *count,
+                           void *stream);
+
+/* Predictor for B tokens x [B, d]:
+ *   hid = ReLU(W1 x + b1), logits = W2 hid + b2, mask = logits > t
+ * logits [B, d_ffn] (may be NULL), mask [B, d_ffn] (may be NULL) and
+ * union_mask [d_ffn] = OR over the batch (may be NULL).  x64 page list item 2
+ * (a 2-layer MLP predictor); Guide section 3. */
+spffn_status spffn_predict(const spffn_layer *layer, const float *x, int32_t B, float *logits,
+                           uint8_t *mask, uint8_t *union_mask, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Neuron-sparse FFN of B tokens x [B, d] over one neuron set shared by the
+ * batch, written to y [B, d]:
+ *   y_b = sum over active i, ascending, of a_i(x_b) * W_down_t[i]
+ * The set is, in order of precedence:
+ *   mask != NULL            the set entries of mask [d_ffn] (compacted here);
+ *   idx, count != NULL      idx[0 .. *count), ascending, each in [0, d_ffn),
+ *                           count a device int32 <= d_ffn;
+ *   all NULL                every neuron (the dense FFN, same kernels).
+ * Guide "The Hidden Inefficiency" (FFN equation) and Step 3 (gather active
+ * rows of W_up, activate, gather the matching columns of W_down, sum).  The
+ * result does not depend on the run: no atomics carry data, and partial sums
+ * are reduced in a fixed order. */
+spffn_status spffn_forward(const spffn_layer *layer, const float *x, int32_t B,
+                           const uint8_t *mask, const int32_t *idx, const int32_t *count,
+                           float *y, void *ws, size_t ws_bytes, void *stream);
+
+#define SPFFN_DECODE_DENSE 1 /* skip predictor and compaction; every neuron */
+
+/* One decode step through the whole stack for B tokens, all on `stream`
+ * with no host synchronisation.  For each layer l:
+ *   n_b = h_b / sqrt(mean(h_b^2) + rms_eps)            (gainless RMS norm)
+ *   M   = OR over b of the predicted mask of n_b        (union over the batch)
+ *   h_b = h_b + FFN_l over M of n_b
+ * x [B, d] is the input residual stream, h [B, d] receives the output (x == h
+ * updates in place).  layer_counts [L] (device int32, may be NULL) receives
+ * |M| per layer; trace may be NULL.  flags: 0 or SPFFN_DECODE_DENSE (every
+ * neuron, no predictor: the dense baseline on the same kernels).  The
+ * per-layer pipeline follows the Guide's section 3 latency-hiding pipeline
+ * (predictor, then the fused neuron-sparse GEMV); the residual/normalisation
+ * glue between layers is this library's reading, as the pages show one layer. */
+spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *h, int32_t B,
+                               int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* ---- load-time utilities ---------------------------------------------- */
+
+/* Activation profile over N tokens x [N, d] (N >= 1): counts[i] (device
+ * int32 [d_ffn]) += the number of tokens with a positive pre-activation of
+ * neuron i (W_gate for ReGLU, W_up for ReLU, plus bias).  Accumulates, so the
+ * caller zeroes counts first.  Guide Step 1 "Offline Activation Profiler". */
+spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, int32_t *counts,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Hot-first order of n neurons from their counts: perm[k] = the neuron of
+ * rank k when sorted by count descending, ties by ascending index (a stable
+ * order, so the result is unique).  Guide Step 1 sorts by descending count. */
+spffn_status spffn_hot_first_order(const int32_t *counts, int32_t n, int32_t *perm,
+                                   void *stream);
+
+/* dst row k = src row perm[k] for k < rows; rows of row_bytes bytes (a
+ * multiple of 4).  perm must be a permutation of 0..rows-1 (an entry outside
+ * that range leaves its dst row unwritten).  src and dst must not overlap.  Applied at load to W_gate,
+ * W_up, W_down_t, b_act, p_w2 and p_b2 together (the Guide's section 2
+ * placement by neuron temperature, kept here as a storage order). */
+spffn_status spffn_permute_rows(const void *src, void *dst, const int32_t *perm, int32_t rows,
+                                int64_t row_bytes, void *stream);
+
+/* 4-bit block split.  aos [rows, cols/32] blocks of 18 bytes: an fp16 scale
+ * (2 bytes, little-endian), then 16 bytes where byte k holds code k in its
+ * low nibble and code k+16 in its high nibble; weight = (code - 8) * scale.
+ * soa (same total size, rows*cols/32*18 bytes, 16-byte aligned) receives the
+ * codes of every block, 16 bytes each, row-major ([rows, cols/2] bytes, same
+ * nibble order), followed by the scales ([rows, cols/32] fp16).  cols % 32
+ * == 0.  The split layout is what SPFFN_Q4_0 weight pointers refer to. */
+spffn_status spffn_q4_0_repack(const void *aos, void *soa, int32_t rows, int32_t cols,
+                               void *stream);
+
+/* [host] Text of the calling thread's last non-OK status ("" if none). */
+const char *spffn_last_error(void);
+
+/* [host] Library version string. */
+const char *spffn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPFFN_H */

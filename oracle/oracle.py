@@ -160,13 +160,15 @@ def union(masks):
 
 
 def logit_threshold(tau):
-    """t = ln(tau / (1 - tau)) in binary64, rounded once to binary32.
+    """t = ln(tau / (1 - tau)) in binary64 from tau as a binary32 value (the
+    precision a layer carries it in), rounded once to binary32.
 
     [Guide] section 3 thresholds sigmoid(logit) > tau; sigmoid is increasing,
     so the same neurons satisfy logit > t."""
-    if not 0.0 < tau < 1.0:
+    tau32 = float(np.float32(tau))
+    if not 0.0 < tau32 < 1.0:
         raise ValueError("tau must lie in (0, 1)")
-    return float(np.float32(math.log(tau / (1.0 - tau))))
+    return float(np.float32(math.log(tau32 / (1.0 - tau32))))
 
 
 # --------------------------------------------------------------------------- #
