@@ -39,7 +39,8 @@ class LayerDesc(C.Structure):
 
 
 class Trace(C.Structure):
-    _fields_ = [("h_in", C.c_void_p), ("union_mask", C.c_void_p), ("logits", C.c_void_p)]
+    _fields_ = [("h_in", C.c_void_p), ("union_mask", C.c_void_p), ("logits", C.c_void_p),
+                ("events", C.c_void_p)]
 
 
 # exported C symbols and their signatures (restype, argtypes)
@@ -277,7 +278,8 @@ def forward(layer, x, mask=None, idx=None, count=None, y=None, ws=None):
 def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws=None):
     """One pass of the whole stack: returns h [B, d].  `trace` is an optional
     dict with device tensors h_in [L, B, d] f32, union_mask [sum d_ffn] u8,
-    logits [sum B*d_ffn] f32."""
+    logits [sum B*d_ffn] f32, and `events`, a ctypes array of 2L hipEvent_t
+    handles recorded around each layer's largest kernel."""
     x = _dev(x, torch.float32, "x")
     B = x.shape[0] if x.dim() == 2 else 1
     if h is None:
@@ -286,8 +288,10 @@ def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws
     _dev(layer_counts, torch.int32, "layer_counts")
     tr = None
     if trace is not None:
+        ev = trace.get("events")
         tr = Trace(h_in=_ptr(trace.get("h_in")), union_mask=_ptr(trace.get("union_mask")),
-                   logits=_ptr(trace.get("logits")))
+                   logits=_ptr(trace.get("logits")),
+                   events=None if ev is None else C.cast(ev, C.c_void_p))
     ws = model.workspace(B) if ws is None else ws
     _check(load().spffn_decode_step(model.handle, _ptr(x), _ptr(h), B,
                                     DECODE_DENSE if dense else 0, _ptr(layer_counts),

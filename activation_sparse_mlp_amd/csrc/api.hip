@@ -20,6 +20,7 @@ struct spffn_model {
     std::vector<const spffn_layer *> layers;
     float eps;
     int d;
+    bool uniform;  // every layer has the same shapes and storage types
 };
 
 namespace {
@@ -56,15 +57,17 @@ WMat wmat(const void *p, int dtype, int rows, int cols) {
     WMat w{};
     w.data = static_cast<const uint8_t *>(p);
     w.scales = nullptr;
+    w.stride = dtype == SPFFN_F32 ? (size_t)cols * 4 : dtype == SPFFN_F16 ? (size_t)cols * 2
+                                                                           : (size_t)cols / 2;
     if (dtype == SPFFN_Q4_0 && p)
         w.scales = reinterpret_cast<const uint16_t *>(w.data + (size_t)rows * (cols / 2));
     return w;
 }
 
 struct Ws {
-    float *n, *hid, *act, *part;
+    float *n, *hid, *act, *part, *scale, *lst_a;
     uint8_t *mask, *uni;
-    int32_t *idx, *count;
+    int32_t *idx, *count, *gcnt, *lst_i;
     int chunks;
 };
 
@@ -78,7 +81,11 @@ Ws carve(const Layer &L, int B, void *ws) {
     w.uni = base + lo.uni;
     w.idx = reinterpret_cast<int32_t *>(base + lo.idx);
     w.count = reinterpret_cast<int32_t *>(base + lo.count);
+    w.scale = reinterpret_cast<float *>(base + lo.scale);
     w.act = reinterpret_cast<float *>(base + lo.act);
+    w.gcnt = reinterpret_cast<int32_t *>(base + lo.gcnt);
+    w.lst_i = reinterpret_cast<int32_t *>(base + lo.lst_i);
+    w.lst_a = reinterpret_cast<float *>(base + lo.lst_a);
     w.part = reinterpret_cast<float *>(base + lo.part);
     w.chunks = lo.chunks;
     return w;
@@ -98,21 +105,48 @@ spffn_status check_ws(size_t need, const void *ws, size_t ws_bytes) {
     return SPFFN_OK;
 }
 
+bool single(const Layer &L, int B) { return B == 1 && b1_fits(L); }
+
 // The FFN part of one layer for B tokens over (idx, count) or every neuron.
-spffn_status run_ffn(const Layer &L, const float *x, int B, const int32_t *idx,
-                     const int32_t *count, const float *resid, float *y, const Ws &w,
-                     hipStream_t s) {
+// x is normalised by `scale` (device, per token) when scale != nullptr; the
+// output is written to y, plus resid when resid != nullptr.
+spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
+                     const int32_t *idx, const int32_t *count, const float *resid, float *y,
+                     const Ws &w, hipStream_t s) {
+    if (single(L, B)) {
+        SPFFN_HIP(launch_up_b1(L, x, scale, idx, count, w.act, s), "gather up/gate launch");
+        SPFFN_HIP(launch_down_b1(L, idx, count, w.act, w.part, w.chunks, s), "gather down launch");
+        SPFFN_HIP(launch_reduce_groups(w.part, w.chunks, L.desc.d, resid, y, s), "reduce launch");
+        return SPFFN_OK;
+    }
+    // the batched kernels take an already normalised input (scale unused)
     SPFFN_HIP(launch_ffn_up(L, x, B, idx, count, w.act, s), "gather up/gate launch");
     SPFFN_HIP(launch_ffn_down(L, B, idx, count, w.act, w.part, w.chunks, s),
               "gather down launch");
-    SPFFN_HIP(launch_reduce(w.part, w.chunks, B, L.desc.d, resid, y, s), "reduce launch");
+    SPFFN_HIP(launch_reduce_groups(w.part, w.chunks, (int64_t)B * L.desc.d, resid, y, s),
+              "reduce launch");
     return SPFFN_OK;
 }
 
-spffn_status run_predict(const Layer &L, const float *x, int B, float *logits, uint8_t *mask,
-                         uint8_t *uni, const Ws &w, hipStream_t s) {
+// Predictor of B tokens.  normalize: x is the residual stream and is RMS
+// normalised first (decode); the RMS scale goes to w.scale.
+spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, float eps,
+                         float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
-    SPFFN_HIP(launch_gemv_hid(D.p_dtype, L.w1, D.r, D.d, x, B, D.p_b1, w.hid, s),
+    if (single(L, B)) {
+        SPFFN_HIP(launch_w1_b1(L, x, eps, normalize, w.hid, w.scale, s), "predictor layer-1 launch");
+        uint8_t *m = mask ? mask : uni;
+        SPFFN_HIP(launch_w2_b1(L, w.hid, logits, m, s), "predictor layer-2 launch");
+        if (mask && uni)
+            SPFFN_HIP(hipMemcpyAsync(uni, mask, D.d_ffn, hipMemcpyDeviceToDevice, s), "union copy");
+        return SPFFN_OK;
+    }
+    const float *xin = x;
+    if (normalize) {
+        SPFFN_HIP(launch_rmsnorm(x, B, D.d, eps, w.n, s), "rmsnorm launch");
+        xin = w.n;
+    }
+    SPFFN_HIP(launch_gemv_hid(D.p_dtype, L.w1, D.r, D.d, xin, B, D.p_b1, w.hid, s),
               "predictor layer-1 launch");
     SPFFN_HIP(launch_gemv_mask(D.p_dtype, L.w2, D.d_ffn, D.r, w.hid, B, D.p_b2, L.t, logits, mask,
                                uni, s),
@@ -141,8 +175,21 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     off += up256((size_t)D.d_ffn * 4);
     lo.count = off;
     off += 256;
+    lo.scale = off;
+    off += up256((size_t)B * 4);
     lo.act = off;
     off += up256((size_t)B * D.d_ffn * 4);
+    const size_t G = (size_t)fused_groups(L), slots = G * fused_rows_per_group();
+    lo.gcnt = off;
+    off += up256(G * 4);
+    lo.lst_i = off;
+    off += up256(slots * 4);
+    lo.lst_a = off;
+    off += up256(slots * 4);
+    if (B == 1 && b1_fits(L)) {
+        lo.chunks = down_b1_chunks(L);
+        if (fused_fits(L) && fused_chunks(L) > lo.chunks) lo.chunks = fused_chunks(L);
+    }
     lo.part = off;
     off += up256((size_t)lo.chunks * B * D.d * 4);
     lo.total = off;
@@ -150,6 +197,52 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
 }
 
 }  // namespace spffn
+
+namespace {
+
+// One-token decode through a uniform stack, four kernels per layer:
+//   1. predictor layer 1, which also yields the RMS scale of h;
+//   2. predictor layer 2 + threshold + gate/up gather + activation, with
+//      per-workgroup lists of the active neurons;
+//   3. the down projection over those lists into per-chunk partial sums;
+//   4. the fixed-order reduction of the partial sums with the residual add.
+spffn_status decode_one_token(const spffn_model *model, const float *x, float *h,
+                              int32_t *layer_counts, const spffn_trace *trace, void *ws,
+                              hipStream_t s) {
+    const int d = model->d;
+    if (x != h) SPFFN_HIP(launch_copy_words(x, h, d, s), "input copy launch");
+    size_t mask_off = 0, logit_off = 0;
+    for (size_t l = 0; l < model->layers.size(); ++l) {
+        const Layer &L = model->layers[l]->L;
+        const int F = L.desc.d_ffn;
+        Ws w = carve(L, 1, ws);
+        if (trace && trace->h_in)
+            SPFFN_HIP(launch_copy_words(h, trace->h_in + l * (size_t)d, d, s), "trace copy launch");
+        SPFFN_HIP(launch_w1_b1(L, h, model->eps, true, w.hid, w.scale, s),
+                  "predictor layer-1 launch");
+        float *lg = (trace && trace->logits) ? trace->logits + logit_off : nullptr;
+        if (trace && trace->events)
+            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
+        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.gcnt, w.lst_i, w.lst_a, s),
+                  "predictor layer-2 + gather launch");
+        if (trace && trace->events)
+            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
+        if (trace && trace->union_mask)
+            SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
+                                     s),
+                      "trace copy");
+        const int chunks = fused_chunks(L);
+        SPFFN_HIP(launch_down_list_b1(L, w.gcnt, w.lst_i, w.lst_a, w.part, chunks,
+                                      layer_counts ? layer_counts + l : nullptr, s),
+                  "gather down launch");
+        SPFFN_HIP(launch_reduce_groups(w.part, chunks, d, h, h, s), "reduce launch");
+        mask_off += F;
+        logit_off += F;
+    }
+    return SPFFN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -234,6 +327,13 @@ spffn_status spffn_model_create(const spffn_layer *const *layers, int32_t n_laye
     }
     m->eps = rms_eps;
     m->d = d;
+    m->uniform = true;
+    for (int i = 1; i < n_layers; ++i) {
+        const spffn_layer_desc &a = layers[0]->L.desc, &b = layers[i]->L.desc;
+        if (a.d_ffn != b.d_ffn || a.r != b.r || a.kind != b.kind || a.w_dtype != b.w_dtype ||
+            a.p_dtype != b.p_dtype)
+            m->uniform = false;
+    }
     *out = m;
     return SPFFN_OK;
 }
@@ -282,12 +382,12 @@ spffn_status spffn_predict(const spffn_layer *layer, const float *x, int32_t B, 
         return fail(SPFFN_E_ARG, "predict: logits, mask and union_mask are all NULL");
     spffn_status st = check_batch(B);
     if (st) return st;
-    if (!aligned(x, 4) || (logits && !aligned(logits, 4)))
-        return fail(SPFFN_E_ARG, "predict: misaligned x or logits");
+    if (!aligned(x, 16) || (logits && !aligned(logits, 4)))
+        return fail(SPFFN_E_ARG, "predict: x must be 16-byte aligned, logits 4-byte");
     const Layer &L = layer->L;
     if ((st = check_ws(layer_ws_layout(L, B).total, ws, ws_bytes))) return st;
     Ws w = carve(L, B, ws);
-    return run_predict(L, x, B, logits, mask, union_mask, w, (hipStream_t)stream);
+    return run_predict(L, x, B, false, 0.0f, logits, mask, union_mask, w, (hipStream_t)stream);
 }
 
 spffn_status spffn_forward(const spffn_layer *layer, const float *x, int32_t B,
@@ -296,7 +396,8 @@ spffn_status spffn_forward(const spffn_layer *layer, const float *x, int32_t B,
     if (!layer || !x || !y) return fail(SPFFN_E_ARG, "forward: NULL layer, x or y");
     spffn_status st = check_batch(B);
     if (st) return st;
-    if (!aligned(x, 4) || !aligned(y, 4)) return fail(SPFFN_E_ARG, "forward: misaligned x or y");
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return fail(SPFFN_E_ARG, "forward: x and y must be 16-byte aligned");
     if (!mask && (idx != nullptr) != (count != nullptr))
         return fail(SPFFN_E_ARG, "forward: idx and count must be given together");
     if (!mask && idx && (!aligned(idx, 4) || !aligned(count, 4)))
@@ -311,7 +412,7 @@ spffn_status spffn_forward(const spffn_layer *layer, const float *x, int32_t B,
         use_idx = w.idx;
         use_count = w.count;
     }
-    return run_ffn(L, x, B, use_idx, use_count, nullptr, y, w, s);
+    return run_ffn(L, x, nullptr, B, use_idx, use_count, nullptr, y, w, s);
 }
 
 spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *h, int32_t B,
@@ -321,12 +422,17 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
     spffn_status st = check_batch(B);
     if (st) return st;
     if (flags & ~SPFFN_DECODE_DENSE) return fail(SPFFN_E_ARG, "decode_step: unknown flags");
-    if (!aligned(x, 4) || !aligned(h, 4) || (layer_counts && !aligned(layer_counts, 4)))
-        return fail(SPFFN_E_ARG, "decode_step: misaligned pointer");
+    if (!aligned(x, 16) || !aligned(h, 16) || (layer_counts && !aligned(layer_counts, 4)))
+        return fail(SPFFN_E_ARG, "decode_step: x and h must be 16-byte aligned");
     if ((st = check_ws(spffn_model_workspace_bytes(model, B), ws, ws_bytes))) return st;
     const bool dense = flags & SPFFN_DECODE_DENSE;
     hipStream_t s = (hipStream_t)stream;
     const int d = model->d;
+    {
+        const Layer &L0 = model->layers[0]->L;
+        if (B == 1 && !dense && model->uniform && single(L0, 1) && fused_fits(L0))
+            return decode_one_token(model, x, h, layer_counts, trace, ws, s);
+    }
     if (x != h) SPFFN_HIP(launch_copy_words(x, h, (int64_t)B * d, s), "input copy launch");
     size_t mask_off = 0, logit_off = 0;
     for (size_t l = 0; l < model->layers.size(); ++l) {
@@ -336,24 +442,34 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
         if (trace && trace->h_in)
             SPFFN_HIP(launch_copy_words(h, trace->h_in + l * (size_t)B * d, (int64_t)B * d, s),
                       "trace copy launch");
-        SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
         const int32_t *idx = nullptr, *cnt = nullptr;
+        float *lg = (trace && trace->logits) ? trace->logits + logit_off : nullptr;
+        const bool one = single(L, B);
+        // single token: the predictor's first kernel computes the RMS scale and
+        // every kernel normalises on the fly; batches normalise into w.n first
+        const float *xin = one ? h : w.n;
+        if (!one) SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
         if (!dense) {
-            float *lg = (trace && trace->logits) ? trace->logits + logit_off : nullptr;
-            if ((st = run_predict(L, w.n, B, lg, nullptr, w.uni, w, s))) return st;
-            SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s), "compact launch");
+            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s))) return st;
+            SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,
+                                     layer_counts ? layer_counts + l : nullptr),
+                      "compact launch");
             if (trace && trace->union_mask)
                 SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F,
                                          hipMemcpyDeviceToDevice, s),
                           "trace copy");
             idx = w.idx;
             cnt = w.count;
+        } else {
+            if (one) SPFFN_HIP(launch_rms_scale(h, B, d, model->eps, w.scale, s), "rms launch");
             if (layer_counts)
-                SPFFN_HIP(launch_copy_words(w.count, layer_counts + l, 1, s), "count copy launch");
-        } else if (layer_counts) {
-            SPFFN_HIP(launch_fill_i32(layer_counts + l, F, 1, s), "count fill launch");
+                SPFFN_HIP(launch_fill_i32(layer_counts + l, F, 1, s), "count fill launch");
         }
-        if ((st = run_ffn(L, w.n, B, idx, cnt, h, h, w, s))) return st;
+        if (trace && trace->events)
+            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
+        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s))) return st;
+        if (trace && trace->events)
+            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
         mask_off += F;
         logit_off += (size_t)B * F;
     }
@@ -366,7 +482,7 @@ spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, 
     (void)ws_bytes;
     if (!layer || !x || !counts) return fail(SPFFN_E_ARG, "profile: NULL pointer");
     if (N < 1) return fail(SPFFN_E_SHAPE, "profile: N=%d < 1", N);
-    if (!aligned(x, 4) || !aligned(counts, 4)) return fail(SPFFN_E_ARG, "profile: misaligned");
+    if (!aligned(x, 16) || !aligned(counts, 4)) return fail(SPFFN_E_ARG, "profile: misaligned");
     const Layer &L = layer->L;
     const WMat &wa = L.desc.kind == SPFFN_REGLU ? L.gate : L.up;
     SPFFN_HIP(launch_gemv_count(L.desc.w_dtype, wa, L.desc.d_ffn, L.desc.d, x, N, L.desc.b_act,

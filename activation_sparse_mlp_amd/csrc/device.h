@@ -31,7 +31,8 @@ __host__ __device__ __forceinline__ size_t row_bytes(int cols) {
 
 template <int FMT>
 __device__ __forceinline__ const uint4 *row_ptr(const WMat &w, size_t row, int cols) {
-    return reinterpret_cast<const uint4 *>(w.data + row * row_bytes<FMT>(cols));
+    (void)cols;
+    return reinterpret_cast<const uint4 *>(w.data + row * w.stride);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {

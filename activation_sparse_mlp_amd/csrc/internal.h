@@ -20,6 +20,7 @@ enum Fmt : int { kF32 = 0, kF16 = 1, kQ4 = 2 };
 struct WMat {
     const uint8_t *data;     // fp32/fp16 elements, or the 4-bit code region
     const uint16_t *scales;  // 4-bit only: fp16 scale bits [rows, cols/32]
+    size_t stride;           // bytes from one row to the next (data region)
 };
 
 // Host-side layer handle (the C ABI's opaque spffn_layer).
@@ -31,7 +32,7 @@ struct Layer {
 
 // Workspace carve-up for a batch of B tokens.
 struct WsLayout {
-    size_t n, hid, mask, uni, idx, count, act, part, total;
+    size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, part, total;
     int chunks;  // neuron chunks of the down projection (partial-sum slots)
 };
 
@@ -41,7 +42,7 @@ WsLayout layer_ws_layout(const Layer &L, int B);
 hipError_t launch_threshold(const float *logits, int64_t n, float t, uint8_t *mask,
                             hipStream_t s);
 hipError_t launch_compact(const uint8_t *mask, int n, int32_t *idx, int32_t *count,
-                          hipStream_t s);
+                          hipStream_t s, int32_t *count2 = nullptr);
 hipError_t launch_hot_first_order(const int32_t *counts, int n, int32_t *perm, hipStream_t s);
 hipError_t launch_permute_rows(const void *src, void *dst, const int32_t *perm, int rows,
                                int64_t row_bytes, hipStream_t s);
@@ -72,5 +73,33 @@ hipError_t launch_fill_i32(int32_t *p, int32_t v, int n, hipStream_t s);
 hipError_t launch_copy_words(const void *src, void *dst, int64_t n_words, hipStream_t s);
 
 int down_chunks(const Layer &L);
+hipError_t launch_rms_scale(const float *h, int B, int d, float eps, float *scale, hipStream_t s);
+
+// Single-token kernels (kernels_b1.hip); usable when b1_fits(L).
+bool b1_fits(const Layer &L);
+int down_b1_chunks(const Layer &L);
+hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
+                        float *scale_out, hipStream_t s);
+hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t *mask,
+                        hipStream_t s);
+hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, const int32_t *idx,
+                        const int32_t *count, float *act, hipStream_t s);
+hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *count,
+                          const float *act, float *part, int chunks, hipStream_t s);
+hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
+                                float *y, hipStream_t s);
+
+// Fused predictor layer 2 + threshold + gate/up gather and its list-driven
+// down projection (decode, one token).
+bool fused_fits(const Layer &L);
+int fused_groups(const Layer &L);
+int fused_rows_per_group();
+int fused_chunks(const Layer &L);
+hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
+                              float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
+                              float *lst_a, hipStream_t s);
+hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t *lst_i,
+                               const float *lst_a, float *part, int chunks, int32_t *total_out,
+                               hipStream_t s);
 
 }  // namespace spffn

@@ -1,0 +1,908 @@
+// Single-token (batch 1) kernels of the decode path, built for latency on
+// gfx950: every wave issues its weight loads before the block stages the
+// activation vector, so the 128-bit streaming loads overlap the staging and
+// the normalisation; row pointers never wait on LDS.
+//
+//   w1_b1      hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps) or 1
+//   w2_b1      logit = W2 . hid + b2, mask = logit > t
+//   up_b1      act_j = max(z, 0) [* u], z = (W_act[i] . h) * s + b_i, i = idx[j]
+//   down_b1    part[c, slice] = sum over run c of act_j * W_down_t[i, slice]
+//   reduce     y = sum_c part[c] (+ h)
+// (s is the RMS scale; multiplying the dot product by it equals normalising
+// the vector first, up to rounding.)
+#include "device.h"
+
+namespace spffn {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit streaming load: weights are read once per step, so they are marked
+// non-temporal to leave the caches to activations, indices and partial sums.
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Stage one activation vector x[0..d) into the packet-transposed LDS layout
+// (see device.h) with float4 loads, all of a thread's loads in flight at once;
+// returns the thread's partial sum of squares (in a fixed order).
+template <int E>
+__device__ __forceinline__ float stage_vec(const float *__restrict__ x, int d, float *xl) {
+    constexpr int V = 8;
+    const int NP = d / E;
+    const int nunits = d / 4;
+    float ss = 0.0f;
+    for (int base = threadIdx.x; base < nunits; base += blockDim.x * V) {
+        float4 v[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int m = base + u * (int)blockDim.x;
+            if (m < nunits) v[u] = reinterpret_cast<const float4 *>(x)[m];
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int m = base + u * (int)blockDim.x;
+            if (m < nunits) {
+                const int c = 4 * m, p = c / E, g = (c - p * E) >> 2;
+                *reinterpret_cast<float4 *>(xl + (g * NP + p) * 4) = v[u];
+                ss = fmaf(v[u].x, v[u].x, ss);
+                ss = fmaf(v[u].y, v[u].y, ss);
+                ss = fmaf(v[u].z, v[u].z, ss);
+                ss = fmaf(v[u].w, v[u].w, ss);
+            }
+        }
+    }
+    return ss;
+}
+
+// Block-wide sum of one float per thread, same order in every block.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int w = 0; w < nw; ++w) t += red[w];
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// predictor layer 1: one wave per row, 4 rows per block
+// ---------------------------------------------------------------------------
+template <int PF>
+__global__ __launch_bounds__(256) void w1_b1_kernel(WMat w1, int r, int d,
+                                                    const float *__restrict__ h, float eps,
+                                                    int normalize, const float *__restrict__ b1,
+                                                    float *__restrict__ hid,
+                                                    float *__restrict__ scale_out) {
+    constexpr int E = PacketElems<PF>::value;
+    constexpr int U = 16;
+    extern __shared__ float xl[];
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wv;
+    const bool rv = row < r;
+    const int NP = d / E;
+    const uint4 *rp = row_ptr<PF>(w1, rv ? row : 0, d);
+
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int p = u * 64 + lane;
+        raw[u] = (rv && p < NP) ? ld_stream(rp + p) : make_uint4(0, 0, 0, 0);
+    }
+    const float ss = block_sum(stage_vec<E>(h, d, xl), red);  // contains the barrier
+    const float s = normalize ? 1.0f / sqrtf(ss / (float)d + eps) : 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
+
+    float acc[1] = {0.0f};
+    for (int pg = 0; pg < NP; pg += 64 * U) {
+        if (pg > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = pg + u * 64 + lane;
+                raw[u] = (rv && p < NP) ? ld_stream(rp + p) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = pg + u * 64 + lane;
+            if (p < NP) packet_dot<PF, 1>(raw[u], 1.0f, xl, NP, p, nullptr, acc);
+        }
+    }
+    const float v = wave_sum(acc[0]);
+    if (rv && lane == 0) hid[row] = fmaxf(fmaf(v, s, b1 ? b1[row] : 0.0f), 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// predictor layer 2 + threshold: R rows per wave, all their packets in flight
+// ---------------------------------------------------------------------------
+template <int PF, int R>
+__global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
+                                                    const float *__restrict__ hid,
+                                                    const float *__restrict__ b2, float t,
+                                                    float *__restrict__ logits,
+                                                    uint8_t *__restrict__ mask) {
+    constexpr int E = PacketElems<PF>::value;
+    constexpr int PL = 2;  // packets per lane per row per pass
+    extern __shared__ float xl[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * 4 + wv) * R;
+    const int NP = r / E;
+
+    uint4 raw[R][PL];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int p = u * 64 + lane;
+            raw[q][u] = (row0 + q < rows && p < NP)
+                            ? ld_stream(row_ptr<PF>(w2, row0 + q, r) + p)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    stage_vec<E>(hid, r, xl);
+    __syncthreads();
+
+    float acc[R][1];
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc[q][0] = 0.0f;
+    for (int pg = 0; pg < NP; pg += 64 * PL) {
+        if (pg > 0) {
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+#pragma unroll
+                for (int u = 0; u < PL; ++u) {
+                    const int p = pg + u * 64 + lane;
+                    raw[q][u] = (row0 + q < rows && p < NP)
+                                    ? ld_stream(row_ptr<PF>(w2, row0 + q, r) + p)
+                                    : make_uint4(0, 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int p = pg + u * 64 + lane;
+                if (p < NP) packet_dot<PF, 1>(raw[q][u], 1.0f, xl, NP, p, nullptr, acc[q]);
+            }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float v = wave_sum(acc[q][0]);
+        const int row = row0 + q;
+        if (lane == 0 && row < rows) {
+            const float l = v + b2[row];
+            if (logits) logits[row] = l;
+            mask[row] = (uint8_t)(l > t);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// row-gather gate/up GEMV + activation: one wave per listed neuron
+// ---------------------------------------------------------------------------
+struct UpB1Args {
+    WMat wa, wu;
+    const float *bias;
+    int d, d_ffn;
+    const int32_t *idx;    // nullptr: every neuron
+    const int32_t *count;  // device count
+    const float *h;        // [d]
+    const float *scale;    // device RMS scale, or nullptr for 1
+    float *act;            // [d_ffn], entry j of the list
+};
+
+template <int FMT, bool GATED, int U>
+__global__ __launch_bounds__(256) void up_b1_kernel(UpB1Args a) {
+    constexpr int E = PacketElems<FMT>::value;
+    extern __shared__ float smem[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cnt = a.idx ? min(max(*a.count, 0), a.d_ffn) : a.d_ffn;
+    if ((int)blockIdx.x * 4 >= cnt) return;  // block-uniform
+    const int NP = a.d / E;
+    float *xl = smem;
+    float *xsum = smem + a.d;
+    const int stride = gridDim.x * 4;
+
+    int j = blockIdx.x * 4 + wv;
+    int i = -1;
+    if (j < cnt) i = a.idx ? a.idx[j] : j;
+    bool valid = (i >= 0) && (i < a.d_ffn);
+
+    uint4 ra[U], ru[U];
+    float sa[U], su[U];
+    auto load_group = [&](int pg) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = pg + u * 64 + lane;
+            const bool ok = valid && p < NP;
+            ra[u] = ok ? ld_stream(row_ptr<FMT>(a.wa, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+            sa[u] = ok ? packet_scale<FMT>(a.wa, i, a.d, p) : 0.0f;
+            if constexpr (GATED) {
+                ru[u] = ok ? ld_stream(row_ptr<FMT>(a.wu, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+                su[u] = ok ? packet_scale<FMT>(a.wu, i, a.d, p) : 0.0f;
+            }
+        }
+    };
+    load_group(0);
+    stage_vec<E>(a.h, a.d, xl);
+    if constexpr (FMT == kQ4) {
+        __syncthreads();
+        stage_xsum<E, 1>(xl, NP, xsum);
+    }
+    __syncthreads();
+    const float s = a.scale ? *a.scale : 1.0f;
+
+    for (;;) {
+        float za[1] = {0.0f}, zu[1] = {0.0f};
+        for (int pg = 0; pg < NP; pg += 64 * U) {
+            if (pg > 0) load_group(pg);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = pg + u * 64 + lane;
+                if (p < NP) {
+                    packet_dot<FMT, 1>(ra[u], sa[u], xl, NP, p, xsum, za);
+                    if constexpr (GATED) packet_dot<FMT, 1>(ru[u], su[u], xl, NP, p, xsum, zu);
+                }
+            }
+        }
+        if (j < cnt) {
+            const float vz = wave_sum(za[0]);
+            const float vu = GATED ? wave_sum(zu[0]) : 1.0f;
+            if (lane == 0) {
+                float v = 0.0f;
+                if (valid) {
+                    v = fmaxf(fmaf(vz, s, a.bias ? a.bias[i] : 0.0f), 0.0f);
+                    if constexpr (GATED) v *= vu * s;
+                }
+                a.act[j] = v;
+            }
+        }
+        j += stride;
+        if (j >= cnt) break;
+        i = a.idx ? a.idx[j] : j;
+        valid = (i >= 0) && (i < a.d_ffn);
+        load_group(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// column-gather down projection: block (slice, chunk), one packet per lane
+// ---------------------------------------------------------------------------
+struct DownB1Args {
+    WMat wd;
+    int d, d_ffn;
+    const int32_t *idx;
+    const int32_t *count;
+    const float *act;
+    int chunks;
+    float *part;  // [chunks, d]
+};
+
+template <int FMT, int UR>
+__global__ __launch_bounds__(256) void down_b1_kernel(DownB1Args a) {
+    constexpr int E = PacketElems<FMT>::value;
+    __shared__ float red[64 * E];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slice = blockIdx.x, c = blockIdx.y;
+    const int NP = a.d / E;
+    const int p = slice * 64 + lane;
+    const bool pv = p < NP;
+    const int cnt = a.idx ? min(max(*a.count, 0), a.d_ffn) : a.d_ffn;
+    const int per = (cnt + a.chunks - 1) / a.chunks;
+    const int j0 = min(cnt, c * per), j1 = min(cnt, j0 + per);
+
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+
+    // this wave's rows: j0 + wv + 4k; lanes prefetch up to 64 of them at once
+    for (int kb = j0 + wv; kb < j1; kb += 4 * 64) {
+        const int jl = kb + 4 * lane;
+        int my_i = -1;
+        float my_a = 0.0f;
+        if (jl < j1) {
+            const int ii = a.idx ? a.idx[jl] : jl;
+            if (ii >= 0 && ii < a.d_ffn) {
+                my_i = ii;
+                my_a = a.act[jl];
+            }
+        }
+        const int nk = min(64, (j1 - kb + 3) / 4);
+        for (int k0 = 0; k0 < nk; k0 += UR) {
+            uint4 raw[UR];
+            float sc[UR], av[UR];
+            int rowi[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                rowi[u] = __shfl(my_i, k0 + u, 64);
+                av[u] = __shfl(my_a, k0 + u, 64);
+                const bool ok = (k0 + u < nk) && rowi[u] >= 0 && pv;
+                raw[u] = ok ? ld_stream(row_ptr<FMT>(a.wd, rowi[u], a.d) + p) : make_uint4(0, 0, 0, 0);
+                sc[u] = ok ? packet_scale<FMT>(a.wd, rowi[u], a.d, p) : 0.0f;
+                if (!ok) av[u] = 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                float w[E];
+                packet_values<FMT>(raw[u], sc[u], w);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = fmaf(av[u], w[e], acc[e]);
+            }
+        }
+    }
+
+    // fixed-order reduction of the four waves through LDS
+    for (int w = 0; w < 4; ++w) {
+        if (wv == w) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float &rr = red[lane * E + e];
+                rr = (w == 0) ? acc[e] : rr + acc[e];
+            }
+        }
+        __syncthreads();
+    }
+    const int col0 = slice * 64 * E;
+    for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
+        if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = red[t];
+}
+
+// ---------------------------------------------------------------------------
+// y[e] = sum_c part[c * n + e] (+ resid[e]): 32 columns x 8 chunk groups per
+// block; each group sums its chunks in ascending order, then the groups are
+// summed in a fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restrict__ part,
+                                                            int chunks, int64_t n,
+                                                            const float *resid, float *y) {
+    __shared__ float red[8][33];
+    const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int64_t e = (int64_t)blockIdx.x * 32 + col;
+    float s = 0.0f;
+    if (e < n) {
+        constexpr int V = 8;
+        for (int c0 = g; c0 < chunks; c0 += 8 * V) {
+            float v[V];
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const int cc = c0 + 8 * u;
+                v[u] = cc < chunks ? part[(int64_t)cc * n + e] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < V; ++u) s += v[u];
+        }
+    }
+    red[g][col] = s;
+    __syncthreads();
+    if (g == 0 && e < n) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tot += red[k][col];
+        y[e] = resid ? resid[e] + tot : tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fused predictor layer 2 + threshold + gate/up gather (decode, one token)
+//
+// Workgroup g owns the interleaved W2 rows {g + G*k : k < RB} (G workgroups),
+// so the hot-first rows spread one per workgroup.  It computes their logits,
+// writes the mask, lists its active rows in LDS (ascending within the
+// workgroup), and then computes the activation of each listed row with all
+// four waves sharing the row's packets.  Output per workgroup g: cnt[g] and
+// the slots [g*RB, g*RB + cnt[g]) of lst_i / lst_a (neuron, activation).
+// Concatenated in workgroup order, the slots hold every active neuron once.
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+    WMat w2, wa, wu;
+    int d, d_ffn, r;
+    int groups;           // row groups of RB rows (rows interleaved with stride groups)
+    const float *hid;     // [r]
+    const float *b2;      // [d_ffn]
+    float t;
+    const float *bias;    // [d_ffn] or nullptr
+    const float *h;       // [d] residual stream (un-normalised)
+    const float *scale;   // device RMS scale
+    float *logits;        // [d_ffn] or nullptr
+    uint8_t *mask;        // [d_ffn]
+    int32_t *cnt;         // [G]
+    int32_t *lst_i;       // [G*RB]
+    float *lst_a;         // [G*RB]
+};
+
+template <int PF, int FMT, bool GATED, int RW, int RP>
+__global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
+    constexpr int EP = PacketElems<PF>::value;
+    constexpr int E = PacketElems<FMT>::value;
+    constexpr int RB = 4 * RW;     // rows per row group
+    constexpr int PL = 2;          // W2 packets per lane per row (rows of <= 128 packets)
+    constexpr int UA = 4;          // activated-row packets per lane per pass
+    extern __shared__ float smem[];
+    __shared__ uint32_t s_bits[4];
+    __shared__ int s_list[RB];
+    __shared__ float s_part[RB][4][2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int G = a.groups;
+    const int NPr = a.r / EP, NPd = a.d / E;
+    float *xh = smem;            // hid, packet-transposed for the predictor format
+    float *xd = smem + a.r;      // h, packet-transposed for the FFN format
+    float *xs = xd + a.d;        // 4-bit block sums of h
+
+    // W2 rows of row group g for this wave: g + G*(wv + 4*q), q < RW
+    uint4 rc[RW][PL], rn[RW][PL];
+    auto load_group = [&](int g, uint4 (&dst)[RW][PL]) {
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+            const int row = g + G * (wv + 4 * q);
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int p = u * 64 + lane;
+                dst[q][u] = (g < G && row < a.d_ffn && p < NPr)
+                                ? ld_stream(row_ptr<PF>(a.w2, row, a.r) + p)
+                                : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    int g = blockIdx.x;
+    load_group(g, rc);
+    // the activations are staged once; the workgroup then walks its row groups
+    stage_vec<EP>(a.hid, a.r, xh);
+    stage_vec<E>(a.h, a.d, xd);
+    if constexpr (FMT == kQ4) {
+        __syncthreads();
+        stage_xsum<E, 1>(xd, NPd, xs);
+    }
+    __syncthreads();
+    const float s = *a.scale;
+
+    for (; g < G; g += gridDim.x) {
+        // next group's W2 rows go out before this group's gather
+        load_group(g + gridDim.x, rn);
+
+        uint32_t bits = 0;
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+            float acc[1] = {0.0f};
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int p = u * 64 + lane;
+                if (p < NPr) packet_dot<PF, 1>(rc[q][u], 1.0f, xh, NPr, p, nullptr, acc);
+            }
+            const float v = wave_sum(acc[0]);
+            const int row = g + G * (wv + 4 * q);
+            if (row < a.d_ffn) {
+                const float l = v + a.b2[row];
+                const bool m = l > a.t;
+                bits |= (uint32_t)m << q;
+                if (lane == 0) {
+                    if (a.logits) a.logits[row] = l;
+                    a.mask[row] = (uint8_t)m;
+                }
+            }
+        }
+        // list of the group's active rows, ordered by local index k = wv + 4q
+        // (ascending row g + G*k)
+        if (lane == 0) s_bits[wv] = bits;
+        __syncthreads();
+        int n_act = 0;
+        for (int w = 0; w < 4; ++w) n_act += __popc(s_bits[w]);
+        if (threadIdx.x < RB) {
+            const int k = threadIdx.x, wk = k & 3, qk = k >> 2;
+            if ((s_bits[wk] >> qk) & 1u) {
+                int rank = 0;
+                for (int k2 = 0; k2 < k; ++k2) rank += (s_bits[k2 & 3] >> (k2 >> 2)) & 1u;
+                s_list[rank] = g + G * k;
+            }
+        }
+        __syncthreads();
+
+        // activations of the listed rows: the four waves share each row
+        for (int k0 = 0; k0 < n_act; k0 += RP) {
+            uint4 ra[RP][UA], ru[RP][UA];
+            float sa[RP][UA], su[RP][UA];
+#pragma unroll
+            for (int kk = 0; kk < RP; ++kk) {
+                const int k = k0 + kk;
+                const int i = k < n_act ? s_list[k] : -1;
+#pragma unroll
+                for (int u = 0; u < UA; ++u) {
+                    const int p = wv * 64 + lane + 256 * u;
+                    const bool ok = i >= 0 && p < NPd;
+                    ra[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wa, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+                    sa[kk][u] = ok ? packet_scale<FMT>(a.wa, i, a.d, p) : 0.0f;
+                    if constexpr (GATED) {
+                        ru[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wu, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+                        su[kk][u] = ok ? packet_scale<FMT>(a.wu, i, a.d, p) : 0.0f;
+                    }
+                }
+            }
+            float za[RP][1], zu[RP][1];
+#pragma unroll
+            for (int kk = 0; kk < RP; ++kk) za[kk][0] = zu[kk][0] = 0.0f;
+            for (int pb = 0; pb < NPd; pb += 256 * UA) {
+                if (pb > 0) {
+#pragma unroll
+                    for (int kk = 0; kk < RP; ++kk) {
+                        const int k = k0 + kk;
+                        const int i = k < n_act ? s_list[k] : -1;
+#pragma unroll
+                        for (int u = 0; u < UA; ++u) {
+                            const int p = pb + wv * 64 + lane + 256 * u;
+                            const bool ok = i >= 0 && p < NPd;
+                            ra[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wa, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+                            sa[kk][u] = ok ? packet_scale<FMT>(a.wa, i, a.d, p) : 0.0f;
+                            if constexpr (GATED) {
+                                ru[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wu, i, a.d) + p) : make_uint4(0, 0, 0, 0);
+                                su[kk][u] = ok ? packet_scale<FMT>(a.wu, i, a.d, p) : 0.0f;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < RP; ++kk)
+#pragma unroll
+                    for (int u = 0; u < UA; ++u) {
+                        const int p = pb + wv * 64 + lane + 256 * u;
+                        if (p < NPd) {
+                            packet_dot<FMT, 1>(ra[kk][u], sa[kk][u], xd, NPd, p, xs, za[kk]);
+                            if constexpr (GATED) packet_dot<FMT, 1>(ru[kk][u], su[kk][u], xd, NPd, p, xs, zu[kk]);
+                        }
+                    }
+            }
+#pragma unroll
+            for (int kk = 0; kk < RP; ++kk) {
+                const float vz = wave_sum(za[kk][0]);
+                const float vu = GATED ? wave_sum(zu[kk][0]) : 0.0f;
+                if (lane == 0 && k0 + kk < n_act) {
+                    s_part[k0 + kk][wv][0] = vz;
+                    s_part[k0 + kk][wv][1] = vu;
+                }
+            }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < n_act) {
+            const int k = threadIdx.x;
+            const int i = s_list[k];
+            float vz = 0.0f, vu = 0.0f;
+            for (int w = 0; w < 4; ++w) {
+                vz += s_part[k][w][0];
+                vu += s_part[k][w][1];
+            }
+            float v = fmaxf(fmaf(vz, s, a.bias ? a.bias[i] : 0.0f), 0.0f);
+            if constexpr (GATED) v *= vu * s;
+            a.lst_i[g * RB + k] = i;
+            a.lst_a[g * RB + k] = v;
+        }
+        if (threadIdx.x == 0) a.cnt[g] = n_act;
+        __syncthreads();  // s_bits / s_list / s_part are reused by the next group
+#pragma unroll
+        for (int q = 0; q < RW; ++q)
+#pragma unroll
+            for (int u = 0; u < PL; ++u) rc[q][u] = rn[q][u];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down projection over the per-workgroup lists of the fused kernel: block
+// (slice, chunk) takes the lists of workgroups [c*G/C, (c+1)*G/C) in order
+// ---------------------------------------------------------------------------
+struct DownListArgs {
+    WMat wd;
+    int d, d_ffn;
+    const int32_t *cnt;
+    const int32_t *lst_i;
+    const float *lst_a;
+    int G, RB;
+    int chunks;
+    float *part;           // [chunks, d]
+    int32_t *total_out;    // device int32 or nullptr: number of listed rows
+};
+
+template <int FMT, int UR>
+__global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
+    constexpr int E = PacketElems<FMT>::value;
+    __shared__ float red[64 * E];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slice = blockIdx.x, c = blockIdx.y;
+    const int NP = a.d / E;
+    const int p = slice * 64 + lane;
+    const bool pv = p < NP;
+    const int g0 = (int)((int64_t)c * a.G / a.chunks), g1 = (int)((int64_t)(c + 1) * a.G / a.chunks);
+    const int ng = g1 - g0;  // at most 64 (checked by the launcher)
+
+    // per-lane count of workgroup g0 + lane, then an inclusive scan over the wave
+    const int my_cnt = lane < ng ? a.cnt[g0 + lane] : 0;
+    int incl = my_cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    const int T = __shfl(incl, 63, 64);  // rows in this chunk
+    if (a.total_out && slice == 0 && wv == 0) {
+        // whole-layer count: sum of every workgroup's count (block (0, 0) only)
+        if (c == 0) {
+            int tot = 0;
+            for (int gg = lane; gg < a.G; gg += 64) tot += a.cnt[gg];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+            if (lane == 0) *a.total_out = tot;
+        }
+    }
+
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+
+    for (int fb = wv; fb < T; fb += 4 * 64) {
+        // lane l fetches flattened row f = fb + 4l
+        const int f = fb + 4 * lane;
+        // workgroup of f: the number of workgroups whose inclusive count is <= f
+        // (shuffles run on every lane; only lanes with f < T use the result)
+        int seg = 0;
+        for (int q = 0; q < ng; ++q) seg += (__shfl(incl, q, 64) <= f) ? 1 : 0;
+        const int prev = __shfl(incl, seg > 0 ? seg - 1 : 0, 64);
+        const int before = seg > 0 ? prev : 0;
+        int my_i = -1;
+        float my_a = 0.0f;
+        if (f < T && seg < ng) {
+            const int slot = (g0 + seg) * a.RB + (f - before);
+            my_i = a.lst_i[slot];
+            my_a = a.lst_a[slot];
+            if (my_i < 0 || my_i >= a.d_ffn) my_i = -1;
+        }
+        const int nk = min(64, (T - fb + 3) / 4);
+        for (int k0 = 0; k0 < nk; k0 += UR) {
+            uint4 raw[UR];
+            float sc[UR], av[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int ri = __shfl(my_i, k0 + u, 64);
+                av[u] = __shfl(my_a, k0 + u, 64);
+                const bool ok = (k0 + u < nk) && ri >= 0 && pv;
+                raw[u] = ok ? ld_stream(row_ptr<FMT>(a.wd, ri, a.d) + p) : make_uint4(0, 0, 0, 0);
+                sc[u] = ok ? packet_scale<FMT>(a.wd, ri, a.d, p) : 0.0f;
+                if (!ok) av[u] = 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                float w[E];
+                packet_values<FMT>(raw[u], sc[u], w);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = fmaf(av[u], w[e], acc[e]);
+            }
+        }
+    }
+
+    for (int w = 0; w < 4; ++w) {
+        if (wv == w) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float &rr = red[lane * E + e];
+                rr = (w == 0) ? acc[e] : rr + acc[e];
+            }
+        }
+        __syncthreads();
+    }
+    const int col0 = slice * 64 * E;
+    for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
+        if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = red[t];
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+// The single-token kernels keep one activation vector in LDS.
+bool b1_fits(const Layer &L) {
+    const int d = L.desc.d;
+    const int E = packet_elems(L.desc.w_dtype);
+    const size_t lds = (size_t)d * 4 + (L.desc.w_dtype == SPFFN_Q4_0 ? (size_t)(d / E) * 4 : 0);
+    return lds <= 56 * 1024 && (size_t)L.desc.r * 4 <= 56 * 1024;
+}
+
+hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
+                        float *scale_out, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    const int blocks = (D.r + 3) / 4;
+    const size_t lds = (size_t)D.d * 4;
+    if (D.p_dtype == SPFFN_F16)
+        w1_b1_kernel<kF16><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
+                                                    scale_out);
+    else
+        w1_b1_kernel<kF32><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
+                                                    scale_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t *mask,
+                        hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    constexpr int R = 8;
+    const int blocks = (D.d_ffn + 4 * R - 1) / (4 * R);
+    const size_t lds = (size_t)D.r * 4;
+    if (D.p_dtype == SPFFN_F16)
+        w2_b1_kernel<kF16, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, logits,
+                                                       mask);
+    else
+        w2_b1_kernel<kF32, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, logits,
+                                                       mask);
+    return hipGetLastError();
+}
+
+constexpr int kUpB1MaxBlocks = 1024;
+
+hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, const int32_t *idx,
+                        const int32_t *count, float *act, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    UpB1Args a{};
+    const bool gated = D.kind == SPFFN_REGLU;
+    a.wa = gated ? L.gate : L.up;
+    a.wu = L.up;
+    a.bias = D.b_act;
+    a.d = D.d;
+    a.d_ffn = D.d_ffn;
+    a.idx = idx;
+    a.count = count;
+    a.h = h;
+    a.scale = scale;
+    a.act = act;
+    int blocks = (D.d_ffn + 3) / 4;
+    if (blocks > kUpB1MaxBlocks) blocks = kUpB1MaxBlocks;
+    const int E = packet_elems(D.w_dtype);
+    const size_t lds = (size_t)D.d * 4 + (D.w_dtype == SPFFN_Q4_0 ? (size_t)(D.d / E) * 4 : 0);
+    switch (D.w_dtype) {
+        case SPFFN_F32:
+            if (gated) up_b1_kernel<kF32, true, 8><<<blocks, 256, lds, s>>>(a);
+            else up_b1_kernel<kF32, false, 8><<<blocks, 256, lds, s>>>(a);
+            break;
+        case SPFFN_F16:
+            if (gated) up_b1_kernel<kF16, true, 8><<<blocks, 256, lds, s>>>(a);
+            else up_b1_kernel<kF16, false, 8><<<blocks, 256, lds, s>>>(a);
+            break;
+        default:
+            if (gated) up_b1_kernel<kQ4, true, 4><<<blocks, 256, lds, s>>>(a);
+            else up_b1_kernel<kQ4, false, 8><<<blocks, 256, lds, s>>>(a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+int down_b1_chunks(const Layer &L) {
+    const int E = packet_elems(L.desc.w_dtype);
+    const int slices = (L.desc.d / E + 63) / 64;
+    int c = 2048 / slices;
+    if (c > 64) c = 64;
+    if (c < 16) c = 16;
+    return c;
+}
+
+hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *count,
+                          const float *act, float *part, int chunks, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    DownB1Args a{};
+    a.wd = L.down;
+    a.d = D.d;
+    a.d_ffn = D.d_ffn;
+    a.idx = idx;
+    a.count = count;
+    a.act = act;
+    a.chunks = chunks;
+    a.part = part;
+    const int E = packet_elems(D.w_dtype);
+    dim3 grid((D.d / E + 63) / 64, chunks);
+    switch (D.w_dtype) {
+        case SPFFN_F32: down_b1_kernel<kF32, 16><<<grid, 256, 0, s>>>(a); break;
+        case SPFFN_F16: down_b1_kernel<kF16, 16><<<grid, 256, 0, s>>>(a); break;
+        default: down_b1_kernel<kQ4, 8><<<grid, 256, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+constexpr int kFusedRW = 4;            // W2 rows per wave in the fused kernel
+constexpr int kFusedWorkgroups = 1 << 20;  // cap on workgroups (each walks groups g, g + grid, ...)
+
+int fused_groups(const Layer &L) { return (L.desc.d_ffn + 4 * kFusedRW - 1) / (4 * kFusedRW); }
+int fused_rows_per_group() { return 4 * kFusedRW; }
+// chunks of the list-driven down projection: 64, or more so that a chunk
+// spans at most 64 workgroups (one per lane of the prefix scan), never more
+// chunks than workgroups
+int fused_chunks(const Layer &L) {
+    const int G = fused_groups(L);
+    int c = (G + 63) / 64;
+    if (c < 64) c = 64;
+    return c < G ? c : G;
+}
+
+bool fused_fits(const Layer &L) {
+    // a W2 row must fit one pass of 2 packets per lane
+    if (L.desc.r / packet_elems(L.desc.p_dtype) > 128) return false;
+    const int E = packet_elems(L.desc.w_dtype);
+    const size_t lds = (size_t)L.desc.r * 4 + (size_t)L.desc.d * 4 +
+                       (L.desc.w_dtype == SPFFN_Q4_0 ? (size_t)(L.desc.d / E) * 4 : 0);
+    return lds <= 56 * 1024;
+}
+
+hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
+                              float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
+                              float *lst_a, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    FusedArgs a{};
+    const bool gated = D.kind == SPFFN_REGLU;
+    a.w2 = L.w2;
+    a.wa = gated ? L.gate : L.up;
+    a.wu = L.up;
+    a.d = D.d;
+    a.d_ffn = D.d_ffn;
+    a.r = D.r;
+    a.hid = hid;
+    a.b2 = D.p_b2;
+    a.t = L.t;
+    a.bias = D.b_act;
+    a.h = h;
+    a.scale = scale;
+    a.logits = logits;
+    a.mask = mask;
+    a.cnt = cnt;
+    a.lst_i = lst_i;
+    a.lst_a = lst_a;
+    const int G = fused_groups(L);
+    a.groups = G;
+    const int E = packet_elems(D.w_dtype);
+    const size_t lds = (size_t)D.r * 4 + (size_t)D.d * 4 +
+                       (D.w_dtype == SPFFN_Q4_0 ? (size_t)(D.d / E) * 4 : 0);
+    constexpr int RW = kFusedRW;
+    // one workgroup per row group unless capped; a capped grid makes each
+    // workgroup stage the activations once and walk several row groups
+    const int nwg = G < kFusedWorkgroups ? G : kFusedWorkgroups;
+#define SPFFN_FUSED(PF, FMT)                                                              \
+    do {                                                                                  \
+        if (gated) pred2_up_b1_kernel<PF, FMT, true, RW, 2><<<nwg, 256, lds, s>>>(a);     \
+        else pred2_up_b1_kernel<PF, FMT, false, RW, 4><<<nwg, 256, lds, s>>>(a);          \
+    } while (0)
+    if (D.p_dtype == SPFFN_F16) {
+        if (D.w_dtype == SPFFN_F16) SPFFN_FUSED(kF16, kF16);
+        else if (D.w_dtype == SPFFN_F32) SPFFN_FUSED(kF16, kF32);
+        else SPFFN_FUSED(kF16, kQ4);
+    } else {
+        if (D.w_dtype == SPFFN_F16) SPFFN_FUSED(kF32, kF16);
+        else if (D.w_dtype == SPFFN_F32) SPFFN_FUSED(kF32, kF32);
+        else SPFFN_FUSED(kF32, kQ4);
+    }
+#undef SPFFN_FUSED
+    return hipGetLastError();
+}
+
+hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t *lst_i,
+                               const float *lst_a, float *part, int chunks, int32_t *total_out,
+                               hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    DownListArgs a{};
+    a.wd = L.down;
+    a.d = D.d;
+    a.d_ffn = D.d_ffn;
+    a.cnt = cnt;
+    a.lst_i = lst_i;
+    a.lst_a = lst_a;
+    a.G = fused_groups(L);
+    a.RB = fused_rows_per_group();
+    a.chunks = chunks;
+    a.part = part;
+    a.total_out = total_out;
+    const int E = packet_elems(D.w_dtype);
+    dim3 grid((D.d / E + 63) / 64, chunks);
+    switch (D.w_dtype) {
+        case SPFFN_F32: down_list_b1_kernel<kF32, 16><<<grid, 256, 0, s>>>(a); break;
+        case SPFFN_F16: down_list_b1_kernel<kF16, 16><<<grid, 256, 0, s>>>(a); break;
+        default: down_list_b1_kernel<kQ4, 8><<<grid, 256, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
+                                float *y, hipStream_t s) {
+    reduce_groups_kernel<<<(int)((n + 31) / 32), 256, 0, s>>>(part, chunks, n, resid, y);
+    return hipGetLastError();
+}
+
+}  // namespace spffn

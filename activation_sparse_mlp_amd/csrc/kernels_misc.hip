@@ -64,33 +64,79 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds_waves, int *
     return lds_waves[wv] + incl - v;
 }
 
+// Register path: when every thread's range is at most kCompactWords 16-byte
+// words, the words are loaded once (all loads in flight), counted, and the
+// indices are written straight from the registers after the scan.
+constexpr int kCompactWords = 4;
+
+__device__ __forceinline__ uint4 load_mask_word(const uint8_t *__restrict__ mask, int i, int end,
+                                                bool vec) {
+    if (vec && i + 16 <= end) return *reinterpret_cast<const uint4 *>(mask + i);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int k = i; k < min(end, i + 16); ++k)
+        w[(k - i) >> 2] |= (uint32_t)(mask[k] != 0 ? 1u : 0u) << (8 * ((k - i) & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const uint8_t *__restrict__ mask,
                                                                   int n, int32_t *__restrict__ idx,
-                                                                  int32_t *__restrict__ count) {
+                                                                  int32_t *__restrict__ count,
+                                                                  int32_t *__restrict__ count2) {
     __shared__ int lds[65];
     const int64_t per = (((int64_t)n + kCompactThreads - 1) / kCompactThreads + 15) & ~(int64_t)15;
     const int beg = (int)min((int64_t)n, (int64_t)threadIdx.x * per);
     const int end = (int)min((int64_t)n, (int64_t)beg + per);
     const bool vec = ((reinterpret_cast<uintptr_t>(mask) & 15) == 0);
-    int c = 0;
-    for (int i = beg; i < end; i += 16) {
-        if (vec && i + 16 <= end) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(mask + i);
-            c += nonzero_bytes(w.x) + nonzero_bytes(w.y) + nonzero_bytes(w.z) + nonzero_bytes(w.w);
-        } else {
-            for (int k = i; k < min(end, i + 16); ++k) c += (mask[k] != 0);
-        }
-    }
     int total;
-    int o = block_exclusive_scan(c, lds, &total);
-    for (int i = beg; i < end; ++i)
-        if (mask[i]) idx[o++] = i;
-    if (threadIdx.x == 0) *count = total;
+    if (per <= 16 * kCompactWords) {
+        uint4 w[kCompactWords];
+#pragma unroll
+        for (int q = 0; q < kCompactWords; ++q) {
+            const int i = beg + 16 * q;
+            w[q] = i < end ? load_mask_word(mask, i, end, vec) : make_uint4(0, 0, 0, 0);
+        }
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < kCompactWords; ++q)
+            c += nonzero_bytes(w[q].x) + nonzero_bytes(w[q].y) + nonzero_bytes(w[q].z) +
+                 nonzero_bytes(w[q].w);
+        int o = block_exclusive_scan(c, lds, &total);
+#pragma unroll
+        for (int q = 0; q < kCompactWords; ++q) {
+            const uint32_t ws[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = beg + 16 * q + 4 * m + b;
+                    if (i < end && ((ws[m] >> (8 * b)) & 0xFFu)) idx[o++] = i;
+                }
+            }
+        }
+    } else {
+        int c = 0;
+        for (int i = beg; i < end; i += 16) {
+            if (vec && i + 16 <= end) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(mask + i);
+                c += nonzero_bytes(w.x) + nonzero_bytes(w.y) + nonzero_bytes(w.z) +
+                     nonzero_bytes(w.w);
+            } else {
+                for (int k = i; k < min(end, i + 16); ++k) c += (mask[k] != 0);
+            }
+        }
+        int o = block_exclusive_scan(c, lds, &total);
+        for (int i = beg; i < end; ++i)
+            if (mask[i]) idx[o++] = i;
+    }
+    if (threadIdx.x == 0) {
+        *count = total;
+        if (count2) *count2 = total;
+    }
 }
 
 hipError_t launch_compact(const uint8_t *mask, int n, int32_t *idx, int32_t *count,
-                          hipStream_t s) {
-    compact_kernel<<<1, kCompactThreads, 0, s>>>(mask, n, idx, count);
+                          hipStream_t s, int32_t *count2) {
+    compact_kernel<<<1, kCompactThreads, 0, s>>>(mask, n, idx, count, count2);
     return hipGetLastError();
 }
 
@@ -234,6 +280,48 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
 
 hipError_t launch_rmsnorm(const float *h, int B, int d, float eps, float *n, hipStream_t s) {
     rmsnorm_kernel<<<B, 256, 0, s>>>(h, d, eps, n);
+    return hipGetLastError();
+}
+
+// scale[b] = 1 / sqrt(mean(h_b^2) + eps), one workgroup per token, same
+// summation order as the single-token predictor kernel's staging pass
+__global__ __launch_bounds__(256) void rms_scale_kernel(const float *__restrict__ h, int d, float eps,
+                                                        float *__restrict__ scale) {
+    __shared__ float red[4];
+    const float *hb = h + (size_t)blockIdx.x * d;
+    constexpr int V = 8;
+    const int nunits = d / 4;
+    float ss = 0.0f;
+    for (int base = threadIdx.x; base < nunits; base += blockDim.x * V) {
+        float4 v[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int m = base + u * (int)blockDim.x;
+            if (m < nunits) v[u] = reinterpret_cast<const float4 *>(hb)[m];
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int m = base + u * (int)blockDim.x;
+            if (m < nunits) {
+                ss = fmaf(v[u].x, v[u].x, ss);
+                ss = fmaf(v[u].y, v[u].y, ss);
+                ss = fmaf(v[u].z, v[u].z, ss);
+                ss = fmaf(v[u].w, v[u].w, ss);
+            }
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < 4; ++w) t += red[w];
+        scale[blockIdx.x] = 1.0f / sqrtf(t / (float)d + eps);
+    }
+}
+
+hipError_t launch_rms_scale(const float *h, int B, int d, float eps, float *scale, hipStream_t s) {
+    rms_scale_kernel<<<B, 256, 0, s>>>(h, d, eps, scale);
     return hipGetLastError();
 }
 

@@ -110,14 +110,20 @@ typedef struct {
 typedef struct spffn_layer spffn_layer; /* [host] opaque, immutable after create */
 typedef struct spffn_model spffn_model; /* [host] opaque: an ordered layer stack  */
 
-/* [host] Optional per-layer record of a decode step, for tests.  Any member
- * may be NULL.  h_in [L, B, d]: the residual stream entering each layer;
- * union_mask [sum_l d_ffn_l]: each layer's union mask, layers concatenated;
- * logits [sum_l B * d_ffn_l]: each layer's predictor logits [B, d_ffn_l]. */
+/* [host] Optional per-layer record of a decode step, for tests and timing.
+ * Any member may be NULL.  h_in [L, B, d]: the residual stream entering each
+ * layer; union_mask [sum_l d_ffn_l]: each layer's union mask, layers
+ * concatenated; logits [sum_l B * d_ffn_l]: each layer's predictor logits
+ * [B, d_ffn_l]; events [2 L]: hipEvent_t handles (owned by the caller)
+ * recorded on the stream immediately before (2l) and after (2l+1) the layer's
+ * largest kernel, the one that streams predictor layer 2 and gathers the
+ * gate/up rows (single-token path; other paths record around the gate/up
+ * gather). */
 typedef struct {
     float *h_in;
     uint8_t *union_mask;
     float *logits;
+    void **events;
 } spffn_trace;
 
 /* ---- handles --------------------------------------------------------- */

@@ -1,0 +1,111 @@
+"""GPU parity at the workloads' full layer shapes, in the launch configuration
+the benchmark times (decode step, hot-first rows for the 70B shape), checked
+layer by layer against the CPU oracle (teacher forced through the trace).
+Large batches are checked on sampled tokens."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_mlp_amd as spffn
+import oracle
+from tests.gpu_helpers import DEV, REL_L2, check_mask_agreement, np_layer, rel_l2
+from workloads import (FALCON_40B, LLAMA2_7B, LLAMA2_70B, OPT_175B_Q4, make_layer,
+                       make_profile_tokens, make_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _build(cfg, layers, hot_first, n_cal=2048):
+    hosts, gl = [], []
+    calib = make_profile_tokens(cfg.d, 256, seed=1, device=DEV) if hot_first else None
+    for l in range(layers):
+        w = make_layer(cfg, l, seed=0, device=DEV, n_cal=n_cal)
+        if hot_first:
+            w, perm, counts = spffn.hot_first_permute(w, calib)
+            c = counts.cpu().numpy()
+            assert np.array_equal(perm.cpu().numpy(), oracle.hot_first_perm(c))
+        gl.append(spffn.Layer(w))
+        hosts.append(w)
+    return hosts, gl
+
+
+def _decode_check(cfg, B, layers, hot_first, tokens_checked=None):
+    print(f"decode {cfg.name} B={B} layers={layers}", flush=True)
+    hosts, gl = _build(cfg, layers, hot_first)
+    model = spffn.Model(gl, rms_eps=1e-5)
+    F, d = cfg.d_ffn, cfg.d
+    x = make_tokens(d, 1, B, seed=3, device=DEV)[0]
+    trace = dict(h_in=torch.empty(layers, B, d, device=DEV),
+                 union_mask=torch.empty(layers * F, dtype=torch.uint8, device=DEV),
+                 logits=torch.empty(layers * B * F, device=DEV))
+    counts = torch.empty(layers, dtype=torch.int32, device=DEV)
+    h = spffn.decode_step(model, x, layer_counts=counts, trace=trace)
+    torch.cuda.synchronize()
+    h_in = trace["h_in"].cpu().numpy().astype(np.float64)
+    outs = np.concatenate([h_in[1:], h.cpu().numpy()[None].astype(np.float64)])
+    masks = trace["union_mask"].cpu().numpy().reshape(layers, F)
+    lg = trace["logits"].cpu().numpy().reshape(layers, B, F)
+    cnts = counts.cpu().numpy()
+    check = range(B) if tokens_checked is None else tokens_checked
+    for l in range(layers):
+        L = np_layer(hosts[l])
+        U = masks[l]
+        assert cnts[l] == U.sum()
+        # the union is the OR of the per-token decisions on the GPU's own logits
+        assert np.array_equal(U, oracle.union(oracle.threshold(lg[l], L["t"])))
+        for b in check:
+            n = oracle.rmsnorm(h_in[l][b], 1e-5)
+            _, ref_lg, _ = oracle.predict(L, n)
+            assert np.max(np.abs(lg[l][b] - ref_lg)) < 1e-3
+            check_mask_agreement(oracle.threshold(lg[l][b], L["t"]), ref_lg, L["t"])
+            y_ref = oracle.ffn_masked(L, n, U)
+            err = rel_l2(outs[l][b] - h_in[l][b], y_ref)
+            print(f"  layer {l} token {b}: active {int(U.sum())}, rel-L2 {err:.2e}", flush=True)
+            assert err <= REL_L2
+    # the step is bit-stable
+    h2 = spffn.decode_step(model, x)
+    assert torch.equal(h, h2)
+
+
+def test_llama2_70b_decode_b1_hot_first():
+    _decode_check(LLAMA2_70B, 1, 2, hot_first=True)
+
+
+def test_llama2_7b_decode_b1():
+    _decode_check(LLAMA2_7B, 1, 2, hot_first=False)
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_llama2_70b_decode_batched(B):
+    _decode_check(LLAMA2_70B, B, 1, hot_first=True, tokens_checked=[0, B - 1])
+
+
+def test_falcon_40b_decode_b8():
+    _decode_check(FALCON_40B, 8, 1, hot_first=False, tokens_checked=[0, 7])
+
+
+def test_opt_175b_q4_0_decode_b1():
+    _decode_check(OPT_175B_Q4, 1, 1, hot_first=False)
+
+
+def test_opt_175b_q4_0_forward_dense_row_sample():
+    """The dense 4-bit FFN (every neuron) at full shape against the oracle on
+    the same dequantised weights."""
+    cfg = OPT_175B_Q4
+    w = make_layer(cfg, 0, seed=2, device=DEV, n_cal=1024)
+    G = spffn.Layer(w)
+    L = np_layer(w)
+    x = make_tokens(cfg.d, 1, 1, seed=4, device=DEV)[0]
+    # a sampled neuron set: every 97th neuron (keeps the oracle fast)
+    idx = torch.arange(0, cfg.d_ffn, 97, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([idx.numel()], dtype=torch.int32, device=DEV)
+    y = spffn.forward(G, x, idx=idx, count=cnt).cpu().numpy()[0]
+    ref, _ = oracle.ffn_sparse(L, x[0].cpu().numpy(), idx.cpu().numpy())
+    assert rel_l2(y, ref) <= REL_L2
