@@ -221,12 +221,14 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
         SPFFN_HIP(launch_w1_b1(L, h, model->eps, true, w.hid, w.scale, s),
                   "predictor layer-1 launch");
         float *lg = (trace && trace->logits) ? trace->logits + logit_off : nullptr;
-        if (trace && trace->events)
-            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
-        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.gcnt, w.lst_i, w.lst_a, s),
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (trace && trace->events) {
+            e0 = (hipEvent_t)trace->events[2 * l];
+            e1 = (hipEvent_t)trace->events[2 * l + 1];
+        }
+        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.gcnt, w.lst_i, w.lst_a, s,
+                                     e0, e1),
                   "predictor layer-2 + gather launch");
-        if (trace && trace->events)
-            SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
                                      s),

@@ -97,7 +97,8 @@ int fused_rows_per_group();
 int fused_chunks(const Layer &L);
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                               float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
-                              float *lst_a, hipStream_t s);
+                              float *lst_a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                              hipEvent_t ev_stop = nullptr);
 hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t *lst_i,
                                const float *lst_a, float *part, int chunks, int32_t *total_out,
                                hipStream_t s);

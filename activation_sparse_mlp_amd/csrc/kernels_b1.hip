@@ -10,6 +10,8 @@
 //   reduce     y = sum_c part[c] (+ h)
 // (s is the RMS scale; multiplying the dot product by it equals normalising
 // the vector first, up to rounding.)
+#include <hip/hip_ext.h>
+
 #include "device.h"
 
 namespace spffn {
@@ -825,7 +827,8 @@ bool fused_fits(const Layer &L) {
 
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                               float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
-                              float *lst_a, hipStream_t s) {
+                              float *lst_a, hipStream_t s, hipEvent_t ev_start,
+                              hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
     FusedArgs a{};
     const bool gated = D.kind == SPFFN_REGLU;
@@ -855,10 +858,22 @@ hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, 
     // one workgroup per row group unless capped; a capped grid makes each
     // workgroup stage the activations once and walk several row groups
     const int nwg = G < kFusedWorkgroups ? G : kFusedWorkgroups;
+    // with timing events the dispatch itself is timestamped (the events bracket
+    // the kernel's execution, not its launch)
 #define SPFFN_FUSED(PF, FMT)                                                              \
     do {                                                                                  \
-        if (gated) pred2_up_b1_kernel<PF, FMT, true, RW, 2><<<nwg, 256, lds, s>>>(a);     \
-        else pred2_up_b1_kernel<PF, FMT, false, RW, 4><<<nwg, 256, lds, s>>>(a);          \
+        if (ev_start || ev_stop) {                                                        \
+            if (gated)                                                                    \
+                hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, true, RW, 2>, dim3(nwg),  \
+                                      dim3(256), (uint32_t)lds, s, ev_start, ev_stop, 0, a); \
+            else                                                                          \
+                hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, false, RW, 4>, dim3(nwg), \
+                                      dim3(256), (uint32_t)lds, s, ev_start, ev_stop, 0, a); \
+        } else if (gated) {                                                               \
+            pred2_up_b1_kernel<PF, FMT, true, RW, 2><<<nwg, 256, lds, s>>>(a);            \
+        } else {                                                                          \
+            pred2_up_b1_kernel<PF, FMT, false, RW, 4><<<nwg, 256, lds, s>>>(a);           \
+        }                                                                                 \
     } while (0)
     if (D.p_dtype == SPFFN_F16) {
         if (D.w_dtype == SPFFN_F16) SPFFN_FUSED(kF16, kF16);

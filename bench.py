@@ -41,7 +41,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-tokens", type=int, default=256)
     ap.add_argument("--n-cal", type=int, default=4096)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (the library's row "
+                         "permutation with the identity order) three times; used to scale "
+                         "the HBM byte counters of a profiler")
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes):
+    """Three launches of a plain copy of nbytes (reads nbytes, writes nbytes)."""
+    import torch
+
+    import activation_sparse_mlp_amd as spffn
+    rows = 1024
+    row_bytes = nbytes // rows
+    src = torch.ones(rows, row_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    perm = torch.arange(rows, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        spffn.permute_rows(src, perm, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    print(json.dumps({"calibrate_copy_bytes": rows * row_bytes, "launches": 3}), flush=True)
 
 
 def step_bytes(layers, counts, B):
@@ -117,6 +138,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the neuron-sparse FFN "
               "stack fits one MI355X, and this build has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch
