@@ -22,6 +22,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
+# HBM bytes per launch of the dominant kernel, measured with the profiler's
+# FETCH_SIZE / WRITE_SIZE counters (scaled by a plain copy of known size) and
+# stored with a hash of the kernel's sources; used only while they still match.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "pred2_up_b1_llama2_70b_b1_traffic.md")
+KERNEL_SOURCES = ["activation_sparse_mlp_amd/csrc/kernels_b1.hip",
+                  "activation_sparse_mlp_amd/csrc/device.h",
+                  "activation_sparse_mlp_amd/csrc/internal.h"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -92,6 +100,32 @@ def dominant_kernel_bytes(L, u, B):
     n_act = 2 if L.kind == "reglu" else 1
     return (L.d_ffn * (L.r * wp + 4 + 1) + int(u) * (n_act * row + 4 + 8)
             + B * (L.r + L.d) * 4)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, batch):
+    """HBM bytes per launch from the stored counter record, or None when there is
+    none for this workload and batch or the kernel has changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            lines = [l for l in f if l.startswith("traffic_record: ")]
+    except OSError:
+        return None
+    src = kernel_source_hash()
+    for line in lines:
+        rec = json.loads(line[len("traffic_record: "):])
+        if (rec.get("workload") == workload and rec.get("batch") == batch
+                and rec.get("source_sha256") == src):
+            return rec
+    return None
 
 
 class HipEvents:
@@ -230,6 +264,10 @@ def main():
     log(f"[kernel] predictor-2 + gather: {kern_us:.2f} us/launch  {kern_gbs:.0f} GB/s "
         f"({len(k_ms)} launches)")
 
+    traffic = measured_traffic(cfg.name, B) if nl == cfg.layers else None
+    if traffic is None:
+        log("[kernel] no counter record for this kernel source and workload: traffic null")
+
     # ---- dense baseline on the same kernels -------------------------------- #
     dense_ms = None
     if args.dense_steps > 0:
@@ -304,7 +342,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "avg_launch_us": round(kern_us, 3),
             "algorithmic_bytes_per_launch": int(np.mean(k_bytes)),
             "step_achieved_GBps": round(gbs, 1),
