@@ -179,7 +179,7 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     off += up256((size_t)B * 4);
     lo.act = off;
     off += up256((size_t)B * D.d_ffn * 4);
-    const size_t G = (size_t)fused_groups(L), slots = G * fused_rows_per_group();
+    const size_t G = (size_t)fused_groups(L), slots = G * fused_rows_per_group(L);
     lo.gcnt = off;
     off += up256(G * 4);
     lo.lst_i = off;

@@ -162,6 +162,65 @@ __device__ __forceinline__ void packet_dot(const uint4 raw, float scale, const f
     }
 }
 
+// Register-operand forms: the E activation values of a packet are held by the
+// lane itself (x[e] = column e of the packet), with their sum for 4-bit blocks.
+template <int FMT>
+__device__ __forceinline__ void load_packet_x(const float *__restrict__ x, int p,
+                                              float (&xv)[PacketElems<FMT>::value], float &xsum) {
+    constexpr int E = PacketElems<FMT>::value;
+    const float4 *src = reinterpret_cast<const float4 *>(x + (size_t)p * E);
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g) {
+        const float4 v = src[g];
+        xv[4 * g + 0] = v.x;
+        xv[4 * g + 1] = v.y;
+        xv[4 * g + 2] = v.z;
+        xv[4 * g + 3] = v.w;
+    }
+    xsum = 0.0f;
+    if constexpr (FMT == kQ4) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) xsum += xv[e];
+    }
+}
+
+// acc += dot(packet, x) with x in registers.
+template <int FMT>
+__device__ __forceinline__ float packet_dot_reg(const uint4 raw, float scale,
+                                                const float (&xv)[PacketElems<FMT>::value],
+                                                float xsum, float acc) {
+    if constexpr (FMT == kF32) {
+        acc = fmaf(__uint_as_float(raw.x), xv[0], acc);
+        acc = fmaf(__uint_as_float(raw.y), xv[1], acc);
+        acc = fmaf(__uint_as_float(raw.z), xv[2], acc);
+        acc = fmaf(__uint_as_float(raw.w), xv[3], acc);
+        return acc;
+    } else if constexpr (FMT == kF16) {
+        typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+        const half8 h = __builtin_bit_cast(half8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], xv[e], acc);
+        return acc;
+    } else {
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        float sq = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) sq = fmaf((float)((lo >> (8 * n)) & 0xFFu), xv[4 * m + n], sq);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                sq = fmaf((float)((hi >> (8 * n)) & 0xFFu), xv[16 + 4 * m + n], sq);
+        }
+        return fmaf(scale, fmaf(-8.0f, xsum, sq), acc);
+    }
+}
+
 // Unpack one packet into E fp32 weights (used by the down projection, which
 // scales whole rows rather than dotting them).
 template <int FMT>

@@ -93,7 +93,7 @@ hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const 
 // down projection (decode, one token).
 bool fused_fits(const Layer &L);
 int fused_groups(const Layer &L);
-int fused_rows_per_group();
+int fused_rows_per_group(const Layer &L);
 int fused_chunks(const Layer &L);
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                               float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,

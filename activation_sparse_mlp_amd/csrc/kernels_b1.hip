@@ -413,176 +413,154 @@ struct FusedArgs {
     float *lst_a;         // [G*RB]
 };
 
-template <int PF, int FMT, bool GATED, int RW, int RP>
+template <int PF, int FMT, bool GATED, int RW, int UA>
 __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
-    constexpr int RB = 4 * RW;     // rows per row group
+    constexpr int RB = 4 * RW;     // rows per row group (one group per workgroup)
     constexpr int PL = 2;          // W2 packets per lane per row (rows of <= 128 packets)
-    constexpr int UA = 4;          // activated-row packets per lane per pass
-    extern __shared__ float smem[];
     __shared__ uint32_t s_bits[4];
-    __shared__ int s_list[RB];
+    __shared__ int s_list[RB];     // listed rows, ascending
+    __shared__ int s_loc[RB];      // their local index k in the group
+    __shared__ float s_bias[RB];   // bias of every row of the group, by local index
     __shared__ float s_part[RB][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int G = a.groups;
+    const int G = a.groups, g = blockIdx.x;
     const int NPr = a.r / EP, NPd = a.d / E;
-    float *xh = smem;            // hid, packet-transposed for the predictor format
-    float *xd = smem + a.r;      // h, packet-transposed for the FFN format
-    float *xs = xd + a.d;        // 4-bit block sums of h
 
-    // W2 rows of row group g for this wave: g + G*(wv + 4*q), q < RW
-    uint4 rc[RW][PL], rn[RW][PL];
-    auto load_group = [&](int g, uint4 (&dst)[RW][PL]) {
+    // Everything the W2 phase needs is requested up front, straight into
+    // registers: the wave's W2 rows g + G*(wv + 4q), the hid values of the
+    // lane's two packets, the rows' b2 entries (lane q holds row q's) and the
+    // bias of each of the group's rows (into LDS).  Addresses are clamped into
+    // range and out-of-range values discarded, so the loads carry no branches.
+    uint4 rc[RW][PL];
 #pragma unroll
-        for (int q = 0; q < RW; ++q) {
-            const int row = g + G * (wv + 4 * q);
+    for (int q = 0; q < RW; ++q) {
+        const int row = g + G * (wv + 4 * q);
+        const bool rv = row < a.d_ffn;
+        const int rr = rv ? row : a.d_ffn - 1;
 #pragma unroll
-            for (int u = 0; u < PL; ++u) {
-                const int p = u * 64 + lane;
-                dst[q][u] = (g < G && row < a.d_ffn && p < NPr)
-                                ? ld_stream(row_ptr<PF>(a.w2, row, a.r) + p)
-                                : make_uint4(0, 0, 0, 0);
-            }
+        for (int u = 0; u < PL; ++u) {
+            const int p = u * 64 + lane;
+            const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
+            rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
         }
-    };
-    int g = blockIdx.x;
-    load_group(g, rc);
-    // the activations are staged once; the workgroup then walks its row groups
-    stage_vec<EP>(a.hid, a.r, xh);
-    stage_vec<E>(a.h, a.d, xd);
-    if constexpr (FMT == kQ4) {
-        __syncthreads();
-        stage_xsum<E, 1>(xd, NPd, xs);
     }
-    __syncthreads();
+    float hv[PL][EP];
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+        const int p = u * 64 + lane;
+        float unused;
+        load_packet_x<PF>(a.hid, p < NPr ? p : NPr - 1, hv[u], unused);
+    }
+    float b2v;
+    {
+        const int row = g + G * (wv + 4 * (lane < RW ? lane : 0));
+        b2v = a.b2[row < a.d_ffn ? row : a.d_ffn - 1];
+    }
+    if ((int)threadIdx.x < RB) {
+        const int row = g + G * (int)threadIdx.x;
+        s_bias[threadIdx.x] = (a.bias && row < a.d_ffn) ? a.bias[row] : 0.0f;
+    }
     const float s = *a.scale;
 
-    for (; g < G; g += gridDim.x) {
-        // next group's W2 rows go out before this group's gather
-        load_group(g + gridDim.x, rn);
-
-        uint32_t bits = 0;
+    // logits, threshold, mask
+    uint32_t bits = 0;
 #pragma unroll
-        for (int q = 0; q < RW; ++q) {
-            float acc[1] = {0.0f};
+    for (int q = 0; q < RW; ++q) {
+        float acc = 0.0f;
 #pragma unroll
-            for (int u = 0; u < PL; ++u) {
-                const int p = u * 64 + lane;
-                if (p < NPr) packet_dot<PF, 1>(rc[q][u], 1.0f, xh, NPr, p, nullptr, acc);
-            }
-            const float v = wave_sum(acc[0]);
-            const int row = g + G * (wv + 4 * q);
-            if (row < a.d_ffn) {
-                const float l = v + a.b2[row];
-                const bool m = l > a.t;
-                bits |= (uint32_t)m << q;
-                if (lane == 0) {
-                    if (a.logits) a.logits[row] = l;
-                    a.mask[row] = (uint8_t)m;
-                }
+        for (int u = 0; u < PL; ++u)
+            if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
+        const float v = wave_sum(acc);
+        const float bq = __shfl(b2v, q, 64);
+        const int row = g + G * (wv + 4 * q);
+        if (row < a.d_ffn) {
+            const float l = v + bq;
+            const bool m = l > a.t;
+            bits |= (uint32_t)m << q;
+            if (lane == 0) {
+                if (a.logits) a.logits[row] = l;
+                a.mask[row] = (uint8_t)m;
             }
         }
-        // list of the group's active rows, ordered by local index k = wv + 4q
-        // (ascending row g + G*k)
-        if (lane == 0) s_bits[wv] = bits;
-        __syncthreads();
-        int n_act = 0;
-        for (int w = 0; w < 4; ++w) n_act += __popc(s_bits[w]);
-        if (threadIdx.x < RB) {
-            const int k = threadIdx.x, wk = k & 3, qk = k >> 2;
-            if ((s_bits[wk] >> qk) & 1u) {
-                int rank = 0;
-                for (int k2 = 0; k2 < k; ++k2) rank += (s_bits[k2 & 3] >> (k2 >> 2)) & 1u;
-                s_list[rank] = g + G * k;
-            }
-        }
-        __syncthreads();
-
-        // activations of the listed rows: the four waves share each row
-        for (int k0 = 0; k0 < n_act; k0 += RP) {
-            uint4 ra[RP][UA], ru[RP][UA];
-            float sa[RP][UA], su[RP][UA];
-#pragma unroll
-            for (int kk = 0; kk < RP; ++kk) {
-                const int k = k0 + kk;
-                const int i = k < n_act ? s_list[k] : -1;
-#pragma unroll
-                for (int u = 0; u < UA; ++u) {
-                    const int p = wv * 64 + lane + 256 * u;
-                    const bool ok = i >= 0 && p < NPd;
-                    ra[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wa, i, a.d) + p) : make_uint4(0, 0, 0, 0);
-                    sa[kk][u] = ok ? packet_scale<FMT>(a.wa, i, a.d, p) : 0.0f;
-                    if constexpr (GATED) {
-                        ru[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wu, i, a.d) + p) : make_uint4(0, 0, 0, 0);
-                        su[kk][u] = ok ? packet_scale<FMT>(a.wu, i, a.d, p) : 0.0f;
-                    }
-                }
-            }
-            float za[RP][1], zu[RP][1];
-#pragma unroll
-            for (int kk = 0; kk < RP; ++kk) za[kk][0] = zu[kk][0] = 0.0f;
-            for (int pb = 0; pb < NPd; pb += 256 * UA) {
-                if (pb > 0) {
-#pragma unroll
-                    for (int kk = 0; kk < RP; ++kk) {
-                        const int k = k0 + kk;
-                        const int i = k < n_act ? s_list[k] : -1;
-#pragma unroll
-                        for (int u = 0; u < UA; ++u) {
-                            const int p = pb + wv * 64 + lane + 256 * u;
-                            const bool ok = i >= 0 && p < NPd;
-                            ra[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wa, i, a.d) + p) : make_uint4(0, 0, 0, 0);
-                            sa[kk][u] = ok ? packet_scale<FMT>(a.wa, i, a.d, p) : 0.0f;
-                            if constexpr (GATED) {
-                                ru[kk][u] = ok ? ld_stream(row_ptr<FMT>(a.wu, i, a.d) + p) : make_uint4(0, 0, 0, 0);
-                                su[kk][u] = ok ? packet_scale<FMT>(a.wu, i, a.d, p) : 0.0f;
-                            }
-                        }
-                    }
-                }
-#pragma unroll
-                for (int kk = 0; kk < RP; ++kk)
-#pragma unroll
-                    for (int u = 0; u < UA; ++u) {
-                        const int p = pb + wv * 64 + lane + 256 * u;
-                        if (p < NPd) {
-                            packet_dot<FMT, 1>(ra[kk][u], sa[kk][u], xd, NPd, p, xs, za[kk]);
-                            if constexpr (GATED) packet_dot<FMT, 1>(ru[kk][u], su[kk][u], xd, NPd, p, xs, zu[kk]);
-                        }
-                    }
-            }
-#pragma unroll
-            for (int kk = 0; kk < RP; ++kk) {
-                const float vz = wave_sum(za[kk][0]);
-                const float vu = GATED ? wave_sum(zu[kk][0]) : 0.0f;
-                if (lane == 0 && k0 + kk < n_act) {
-                    s_part[k0 + kk][wv][0] = vz;
-                    s_part[k0 + kk][wv][1] = vu;
-                }
-            }
-        }
-        __syncthreads();
-        if ((int)threadIdx.x < n_act) {
-            const int k = threadIdx.x;
-            const int i = s_list[k];
-            float vz = 0.0f, vu = 0.0f;
-            for (int w = 0; w < 4; ++w) {
-                vz += s_part[k][w][0];
-                vu += s_part[k][w][1];
-            }
-            float v = fmaxf(fmaf(vz, s, a.bias ? a.bias[i] : 0.0f), 0.0f);
-            if constexpr (GATED) v *= vu * s;
-            a.lst_i[g * RB + k] = i;
-            a.lst_a[g * RB + k] = v;
-        }
-        if (threadIdx.x == 0) a.cnt[g] = n_act;
-        __syncthreads();  // s_bits / s_list / s_part are reused by the next group
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-#pragma unroll
-            for (int u = 0; u < PL; ++u) rc[q][u] = rn[q][u];
     }
+    // list of the group's active rows, ordered by local index k = wv + 4q
+    // (ascending row g + G*k)
+    if (lane == 0) s_bits[wv] = bits;
+    __syncthreads();
+    int n_act = 0;
+    for (int w = 0; w < 4; ++w) n_act += __popc(s_bits[w]);
+    if (threadIdx.x < RB) {
+        const int k = threadIdx.x, wk = k & 3, qk = k >> 2;
+        if ((s_bits[wk] >> qk) & 1u) {
+            int rank = 0;
+            for (int k2 = 0; k2 < k; ++k2) rank += (s_bits[k2 & 3] >> (k2 >> 2)) & 1u;
+            s_list[rank] = g + G * k;
+            s_loc[rank] = k;
+        }
+    }
+    __syncthreads();
+
+    // activations of the listed rows: the four waves share each row, lane
+    // (wv, lane) always takes packets wv*64 + lane + 256u, so its activation
+    // values are loaded once, into registers, after the first row's weights
+    // have been requested (a group without active rows never reads them)
+    float xv[UA][E], xs[UA];
+    for (int k = 0; k < n_act; ++k) {
+        const int i = s_list[k];
+        uint4 ra[UA], ru[UA];
+        float sa[UA], su[UA];
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+            const int p = wv * 64 + lane + 256 * u;
+            const bool ok = p < NPd;
+            const int pc = ok ? p : NPd - 1;
+            const uint4 va = ld_stream(row_ptr<FMT>(a.wa, i, a.d) + pc);
+            ra[u] = ok ? va : make_uint4(0, 0, 0, 0);
+            sa[u] = ok ? packet_scale<FMT>(a.wa, i, a.d, pc) : 0.0f;
+            if constexpr (GATED) {
+                const uint4 vu = ld_stream(row_ptr<FMT>(a.wu, i, a.d) + pc);
+                ru[u] = ok ? vu : make_uint4(0, 0, 0, 0);
+                su[u] = ok ? packet_scale<FMT>(a.wu, i, a.d, pc) : 0.0f;
+            }
+        }
+        if (k == 0) {
+#pragma unroll
+            for (int u = 0; u < UA; ++u) {
+                const int p = wv * 64 + lane + 256 * u;
+                load_packet_x<FMT>(a.h, p < NPd ? p : NPd - 1, xv[u], xs[u]);
+            }
+        }
+        float za = 0.0f, zu = 0.0f;
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+            if (wv * 64 + lane + 256 * u < NPd) {
+                za = packet_dot_reg<FMT>(ra[u], sa[u], xv[u], xs[u], za);
+                if constexpr (GATED) zu = packet_dot_reg<FMT>(ru[u], su[u], xv[u], xs[u], zu);
+            }
+        }
+        za = wave_sum(za);
+        if constexpr (GATED) zu = wave_sum(zu);
+        if (lane == 0) {
+            s_part[k][wv][0] = za;
+            s_part[k][wv][1] = zu;
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < n_act) {
+        const int k = threadIdx.x;
+        float vz = 0.0f, vu = 0.0f;
+        for (int w = 0; w < 4; ++w) {
+            vz += s_part[k][w][0];
+            vu += s_part[k][w][1];
+        }
+        float v = fmaxf(fmaf(vz, s, s_bias[s_loc[k]]), 0.0f);
+        if constexpr (GATED) v *= vu * s;
+        a.lst_i[g * RB + k] = s_list[k];
+        a.lst_a[g * RB + k] = v;
+    }
+    if (threadIdx.x == 0) a.cnt[g] = n_act;
 }
 
 // ---------------------------------------------------------------------------
@@ -801,14 +779,21 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-constexpr int kFusedRW = 4;            // W2 rows per wave in the fused kernel
-constexpr int kFusedWorkgroups = 1 << 20;  // cap on workgroups (each walks groups g, g + grid, ...)
+// Row groups of the fused kernel: 16 rows per workgroup, or 32 when 16 would
+// need more workgroups than the chip keeps resident at once (4 per CU), so
+// that every group's W2 rows are requested in the kernel's first moments.
+constexpr int kResidentGroups = 1024;
 
-int fused_groups(const Layer &L) { return (L.desc.d_ffn + 4 * kFusedRW - 1) / (4 * kFusedRW); }
-int fused_rows_per_group() { return 4 * kFusedRW; }
-// chunks of the list-driven down projection: 64, or more so that a chunk
-// spans at most 64 workgroups (one per lane of the prefix scan), never more
-// chunks than workgroups
+int fused_rows_per_group(const Layer &L) {
+    return (L.desc.d_ffn + 15) / 16 > kResidentGroups ? 32 : 16;
+}
+int fused_groups(const Layer &L) {
+    const int RB = fused_rows_per_group(L);
+    return (L.desc.d_ffn + RB - 1) / RB;
+}
+
+// Down-projection row chunks over the fused kernel's lists: at most 64 groups
+// per chunk (one wave scans their counts), at least 64 chunks.
 int fused_chunks(const Layer &L) {
     const int G = fused_groups(L);
     int c = (G + 63) / 64;
@@ -816,13 +801,49 @@ int fused_chunks(const Layer &L) {
     return c < G ? c : G;
 }
 
+// Activated-row packets per lane: one pass of 256*UA packets covers a row.
+static int fused_ua(const Layer &L) {
+    const int NPd = L.desc.d / packet_elems(L.desc.w_dtype);
+    return NPd <= 512 ? 2 : NPd <= 1024 ? 4 : 8;
+}
+
 bool fused_fits(const Layer &L) {
-    // a W2 row must fit one pass of 2 packets per lane
-    if (L.desc.r / packet_elems(L.desc.p_dtype) > 128) return false;
-    const int E = packet_elems(L.desc.w_dtype);
-    const size_t lds = (size_t)L.desc.r * 4 + (size_t)L.desc.d * 4 +
-                       (L.desc.w_dtype == SPFFN_Q4_0 ? (size_t)(L.desc.d / E) * 4 : 0);
-    return lds <= 56 * 1024;
+    // a W2 row must fit one pass of 2 packets per lane, an activated row one
+    // pass of 8 packets per lane
+    return L.desc.r / packet_elems(L.desc.p_dtype) <= 128 &&
+           L.desc.d / packet_elems(L.desc.w_dtype) <= 256 * 8;
+}
+
+template <int PF, int FMT, bool GATED, int RW, int UA>
+static void launch_fused_t(const FusedArgs &a, int G, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    // with timing events the dispatch itself is timestamped (the events bracket
+    // the kernel's execution, not its launch)
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, GATED, RW, UA>, dim3(G), dim3(256), 0, s,
+                              e0, e1, 0, a);
+    else
+        pred2_up_b1_kernel<PF, FMT, GATED, RW, UA><<<G, 256, 0, s>>>(a);
+}
+
+template <int PF, int FMT, bool GATED>
+static void launch_fused_rw(const FusedArgs &a, int G, int RB, int UA, hipStream_t s,
+                            hipEvent_t e0, hipEvent_t e1) {
+    if (RB == 32) {
+        if (UA == 2) launch_fused_t<PF, FMT, GATED, 8, 2>(a, G, s, e0, e1);
+        else if (UA == 4) launch_fused_t<PF, FMT, GATED, 8, 4>(a, G, s, e0, e1);
+        else launch_fused_t<PF, FMT, GATED, 8, 8>(a, G, s, e0, e1);
+    } else {
+        if (UA == 2) launch_fused_t<PF, FMT, GATED, 4, 2>(a, G, s, e0, e1);
+        else if (UA == 4) launch_fused_t<PF, FMT, GATED, 4, 4>(a, G, s, e0, e1);
+        else launch_fused_t<PF, FMT, GATED, 4, 8>(a, G, s, e0, e1);
+    }
+}
+
+template <int PF, int FMT>
+static void launch_fused_kind(const FusedArgs &a, bool gated, int G, int RB, int UA, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
+    if (gated) launch_fused_rw<PF, FMT, true>(a, G, RB, UA, s, e0, e1);
+    else launch_fused_rw<PF, FMT, false>(a, G, RB, UA, s, e0, e1);
 }
 
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
@@ -849,42 +870,17 @@ hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, 
     a.cnt = cnt;
     a.lst_i = lst_i;
     a.lst_a = lst_a;
-    const int G = fused_groups(L);
+    const int G = fused_groups(L), RB = fused_rows_per_group(L), UA = fused_ua(L);
     a.groups = G;
-    const int E = packet_elems(D.w_dtype);
-    const size_t lds = (size_t)D.r * 4 + (size_t)D.d * 4 +
-                       (D.w_dtype == SPFFN_Q4_0 ? (size_t)(D.d / E) * 4 : 0);
-    constexpr int RW = kFusedRW;
-    // one workgroup per row group unless capped; a capped grid makes each
-    // workgroup stage the activations once and walk several row groups
-    const int nwg = G < kFusedWorkgroups ? G : kFusedWorkgroups;
-    // with timing events the dispatch itself is timestamped (the events bracket
-    // the kernel's execution, not its launch)
-#define SPFFN_FUSED(PF, FMT)                                                              \
-    do {                                                                                  \
-        if (ev_start || ev_stop) {                                                        \
-            if (gated)                                                                    \
-                hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, true, RW, 2>, dim3(nwg),  \
-                                      dim3(256), (uint32_t)lds, s, ev_start, ev_stop, 0, a); \
-            else                                                                          \
-                hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, false, RW, 4>, dim3(nwg), \
-                                      dim3(256), (uint32_t)lds, s, ev_start, ev_stop, 0, a); \
-        } else if (gated) {                                                               \
-            pred2_up_b1_kernel<PF, FMT, true, RW, 2><<<nwg, 256, lds, s>>>(a);            \
-        } else {                                                                          \
-            pred2_up_b1_kernel<PF, FMT, false, RW, 4><<<nwg, 256, lds, s>>>(a);           \
-        }                                                                                 \
-    } while (0)
     if (D.p_dtype == SPFFN_F16) {
-        if (D.w_dtype == SPFFN_F16) SPFFN_FUSED(kF16, kF16);
-        else if (D.w_dtype == SPFFN_F32) SPFFN_FUSED(kF16, kF32);
-        else SPFFN_FUSED(kF16, kQ4);
+        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF16, kF16>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF16, kF32>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        else launch_fused_kind<kF16, kQ4>(a, gated, G, RB, UA, s, ev_start, ev_stop);
     } else {
-        if (D.w_dtype == SPFFN_F16) SPFFN_FUSED(kF32, kF16);
-        else if (D.w_dtype == SPFFN_F32) SPFFN_FUSED(kF32, kF32);
-        else SPFFN_FUSED(kF32, kQ4);
+        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF32, kF16>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF32, kF32>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        else launch_fused_kind<kF32, kQ4>(a, gated, G, RB, UA, s, ev_start, ev_stop);
     }
-#undef SPFFN_FUSED
     return hipGetLastError();
 }
 
@@ -900,7 +896,7 @@ hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t
     a.lst_i = lst_i;
     a.lst_a = lst_a;
     a.G = fused_groups(L);
-    a.RB = fused_rows_per_group();
+    a.RB = fused_rows_per_group(L);
     a.chunks = chunks;
     a.part = part;
     a.total_out = total_out;
