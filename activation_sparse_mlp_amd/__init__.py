@@ -6,7 +6,7 @@ column-gather down projection -- and a multi-layer decode step, all as
 hand-written HIP kernels.  This package only marshals torch tensors into it.
 """
 from ._lib import (DECODE_DENSE, F16, F32, MAX_BATCH, PERMUTED_KEYS, Q4_0, RELU, REGLU,  # noqa
-                   SIGNATURES, Layer, Model, SpffnError, compact, decode_step, forward,
+                   SIGNATURES, DecodeGraph, Layer, Model, SpffnError, compact, decode_step, forward,
                    hot_first_order, hot_first_permute, load, permute_rows, predict, profile,
                    q4_0_repack, threshold, version)
 

@@ -59,6 +59,10 @@ SIGNATURES = {
     "spffn_forward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spffn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(Trace), _vp, _sz,
                                  _vp]),
+    "spffn_decode_graph_create": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz,
+                                         C.POINTER(_vp)]),
+    "spffn_graph_launch": (_i32, [_vp, _vp]),
+    "spffn_graph_destroy": (None, [_vp]),
     "spffn_profile": (_i32, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "spffn_hot_first_order": (_i32, [_vp, _i32, _vp, _vp]),
     "spffn_permute_rows": (_i32, [_vp, _vp, _vp, _i32, _i64, _vp]),
@@ -298,6 +302,40 @@ def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws
                                     C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),
                                     _stream()), "spffn_decode_step")
     return h
+
+
+class DecodeGraph:
+    """One decode step captured into a HIP graph (a spffn_graph handle).
+
+    The graph keeps the addresses of x, h, layer_counts and the workspace, so
+    this object holds references to those tensors; write the next input into
+    `x` and call launch() once per token."""
+
+    def __init__(self, model, x, h=None, dense=False, layer_counts=None, ws=None):
+        x = _dev(x, torch.float32, "x")
+        B = x.shape[0] if x.dim() == 2 else 1
+        if h is None:
+            h = torch.empty_like(x)
+        _dev(h, torch.float32, "h")
+        _dev(layer_counts, torch.int32, "layer_counts")
+        ws = model.workspace(B) if ws is None else ws
+        self.model, self.x, self.h, self.layer_counts, self.ws = model, x, h, layer_counts, ws
+        out = _vp()
+        _check(load().spffn_decode_graph_create(model.handle, _ptr(x), _ptr(h), B,
+                                                DECODE_DENSE if dense else 0, _ptr(layer_counts),
+                                                _ptr(ws), ws.numel(), C.byref(out)),
+               "spffn_decode_graph_create")
+        self.handle = out.value
+
+    def launch(self, stream=None):
+        _check(load().spffn_graph_launch(self.handle, _stream(stream)), "spffn_graph_launch")
+        return self.h
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib = load()
+            _lib.spffn_graph_destroy(self.handle)
+            self.handle = None
 
 
 def profile(layer, x, counts=None):

@@ -244,6 +244,13 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
     return SPFFN_OK;
 }
 
+spffn_status check_decode(const spffn_model *model, const float *x, const float *h, int32_t B,
+                          int32_t flags, const int32_t *layer_counts, const void *ws,
+                          size_t ws_bytes);
+spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, int32_t B,
+                            int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
+                            void *ws, hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -420,15 +427,82 @@ spffn_status spffn_forward(const spffn_layer *layer, const float *x, int32_t B,
 spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *h, int32_t B,
                                int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
                                void *ws, size_t ws_bytes, void *stream) {
+    spffn_status st = check_decode(model, x, h, B, flags, layer_counts, ws, ws_bytes);
+    if (st) return st;
+    return enqueue_decode(model, x, h, B, flags, layer_counts, trace, ws, (hipStream_t)stream);
+}
+
+struct spffn_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+spffn_status spffn_decode_graph_create(const spffn_model *model, const float *x, float *h,
+                                       int32_t B, int32_t flags, int32_t *layer_counts, void *ws,
+                                       size_t ws_bytes, spffn_graph **out) {
+    if (!out) return fail(SPFFN_E_ARG, "decode_graph_create: NULL out");
+    spffn_status st = check_decode(model, x, h, B, flags, layer_counts, ws, ws_bytes);
+    if (st) return st;
+    hipStream_t cs = nullptr;
+    SPFFN_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return fail(SPFFN_E_HIP, "begin capture: %s", hipGetErrorString(e));
+    }
+    st = enqueue_decode(model, x, h, B, flags, layer_counts, nullptr, ws, cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (st) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (e != hipSuccess) return fail(SPFFN_E_HIP, "end capture: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return fail(SPFFN_E_HIP, "graph instantiate: %s", hipGetErrorString(e));
+    }
+    *out = new spffn_graph{graph, exec};
+    return SPFFN_OK;
+}
+
+spffn_status spffn_graph_launch(const spffn_graph *graph, void *stream) {
+    if (!graph) return fail(SPFFN_E_ARG, "graph_launch: NULL graph");
+    SPFFN_HIP(hipGraphLaunch(graph->exec, (hipStream_t)stream), "graph launch");
+    return SPFFN_OK;
+}
+
+void spffn_graph_destroy(spffn_graph *graph) {
+    if (!graph) return;
+    (void)hipGraphExecDestroy(graph->exec);
+    (void)hipGraphDestroy(graph->graph);
+    delete graph;
+}
+
+}  // extern "C"
+
+namespace {
+
+spffn_status check_decode(const spffn_model *model, const float *x, const float *h, int32_t B,
+                          int32_t flags, const int32_t *layer_counts, const void *ws,
+                          size_t ws_bytes) {
     if (!model || !x || !h) return fail(SPFFN_E_ARG, "decode_step: NULL model, x or h");
     spffn_status st = check_batch(B);
     if (st) return st;
     if (flags & ~SPFFN_DECODE_DENSE) return fail(SPFFN_E_ARG, "decode_step: unknown flags");
     if (!aligned(x, 16) || !aligned(h, 16) || (layer_counts && !aligned(layer_counts, 4)))
         return fail(SPFFN_E_ARG, "decode_step: x and h must be 16-byte aligned");
-    if ((st = check_ws(spffn_model_workspace_bytes(model, B), ws, ws_bytes))) return st;
+    return check_ws(spffn_model_workspace_bytes(model, B), ws, ws_bytes);
+}
+
+spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, int32_t B,
+                            int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
+                            void *ws, hipStream_t s) {
+    spffn_status st = SPFFN_OK;
     const bool dense = flags & SPFFN_DECODE_DENSE;
-    hipStream_t s = (hipStream_t)stream;
     const int d = model->d;
     {
         const Layer &L0 = model->layers[0]->L;
@@ -477,6 +551,10 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
     }
     return SPFFN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, int32_t *counts,
                            void *ws, size_t ws_bytes, void *stream) {

@@ -565,7 +565,9 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
 
 // ---------------------------------------------------------------------------
 // down projection over the per-workgroup lists of the fused kernel: block
-// (slice, chunk) takes the lists of workgroups [c*G/C, (c+1)*G/C) in order
+// (slice, chunk c) takes the lists of workgroups c, c + C, c + 2C, ... in that
+// order.  Striding (rather than contiguous ranges) spreads the hot-first rows,
+// which all sit in the first workgroups, evenly over the chunks.
 // ---------------------------------------------------------------------------
 struct DownListArgs {
     WMat wd;
@@ -588,11 +590,11 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
     const int NP = a.d / E;
     const int p = slice * 64 + lane;
     const bool pv = p < NP;
-    const int g0 = (int)((int64_t)c * a.G / a.chunks), g1 = (int)((int64_t)(c + 1) * a.G / a.chunks);
-    const int ng = g1 - g0;  // at most 64 (checked by the launcher)
+    const int C = a.chunks;
+    const int ng = (a.G - c + C - 1) / C;  // groups c + C*j, j < ng; at most 64 (launcher)
 
-    // per-lane count of workgroup g0 + lane, then an inclusive scan over the wave
-    const int my_cnt = lane < ng ? a.cnt[g0 + lane] : 0;
+    // per-lane count of group c + C*lane, then an inclusive scan over the wave
+    const int my_cnt = lane < ng ? a.cnt[c + C * lane] : 0;
     int incl = my_cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
         int my_i = -1;
         float my_a = 0.0f;
         if (f < T && seg < ng) {
-            const int slot = (g0 + seg) * a.RB + (f - before);
+            const int slot = (c + C * seg) * a.RB + (f - before);
             my_i = a.lst_i[slot];
             my_a = a.lst_a[slot];
             if (my_i < 0 || my_i >= a.d_ffn) my_i = -1;
@@ -779,13 +781,15 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-// Row groups of the fused kernel: 16 rows per workgroup, or 32 when 16 would
-// need more workgroups than the chip keeps resident at once (4 per CU), so
-// that every group's W2 rows are requested in the kernel's first moments.
-constexpr int kResidentGroups = 1024;
+// Row groups of the fused kernel: 8 rows per workgroup (two W2 rows per
+// wave).  Small groups keep the kernel at 4-5 resident workgroups per CU and
+// let the hardware hand new groups to CUs whose groups had few active rows,
+// which balances the gather phase better than larger groups.
+constexpr int kFusedRW = 2;
 
 int fused_rows_per_group(const Layer &L) {
-    return (L.desc.d_ffn + 15) / 16 > kResidentGroups ? 32 : 16;
+    (void)L;
+    return 4 * kFusedRW;
 }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
@@ -826,24 +830,18 @@ static void launch_fused_t(const FusedArgs &a, int G, hipStream_t s, hipEvent_t 
 }
 
 template <int PF, int FMT, bool GATED>
-static void launch_fused_rw(const FusedArgs &a, int G, int RB, int UA, hipStream_t s,
-                            hipEvent_t e0, hipEvent_t e1) {
-    if (RB == 32) {
-        if (UA == 2) launch_fused_t<PF, FMT, GATED, 8, 2>(a, G, s, e0, e1);
-        else if (UA == 4) launch_fused_t<PF, FMT, GATED, 8, 4>(a, G, s, e0, e1);
-        else launch_fused_t<PF, FMT, GATED, 8, 8>(a, G, s, e0, e1);
-    } else {
-        if (UA == 2) launch_fused_t<PF, FMT, GATED, 4, 2>(a, G, s, e0, e1);
-        else if (UA == 4) launch_fused_t<PF, FMT, GATED, 4, 4>(a, G, s, e0, e1);
-        else launch_fused_t<PF, FMT, GATED, 4, 8>(a, G, s, e0, e1);
-    }
+static void launch_fused_rw(const FusedArgs &a, int G, int UA, hipStream_t s, hipEvent_t e0,
+                            hipEvent_t e1) {
+    if (UA == 2) launch_fused_t<PF, FMT, GATED, kFusedRW, 2>(a, G, s, e0, e1);
+    else if (UA == 4) launch_fused_t<PF, FMT, GATED, kFusedRW, 4>(a, G, s, e0, e1);
+    else launch_fused_t<PF, FMT, GATED, kFusedRW, 8>(a, G, s, e0, e1);
 }
 
 template <int PF, int FMT>
-static void launch_fused_kind(const FusedArgs &a, bool gated, int G, int RB, int UA, hipStream_t s,
+static void launch_fused_kind(const FusedArgs &a, bool gated, int G, int UA, hipStream_t s,
                               hipEvent_t e0, hipEvent_t e1) {
-    if (gated) launch_fused_rw<PF, FMT, true>(a, G, RB, UA, s, e0, e1);
-    else launch_fused_rw<PF, FMT, false>(a, G, RB, UA, s, e0, e1);
+    if (gated) launch_fused_rw<PF, FMT, true>(a, G, UA, s, e0, e1);
+    else launch_fused_rw<PF, FMT, false>(a, G, UA, s, e0, e1);
 }
 
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
@@ -870,16 +868,16 @@ hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, 
     a.cnt = cnt;
     a.lst_i = lst_i;
     a.lst_a = lst_a;
-    const int G = fused_groups(L), RB = fused_rows_per_group(L), UA = fused_ua(L);
+    const int G = fused_groups(L), UA = fused_ua(L);
     a.groups = G;
     if (D.p_dtype == SPFFN_F16) {
-        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF16, kF16>(a, gated, G, RB, UA, s, ev_start, ev_stop);
-        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF16, kF32>(a, gated, G, RB, UA, s, ev_start, ev_stop);
-        else launch_fused_kind<kF16, kQ4>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF16, kF16>(a, gated, G, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF16, kF32>(a, gated, G, UA, s, ev_start, ev_stop);
+        else launch_fused_kind<kF16, kQ4>(a, gated, G, UA, s, ev_start, ev_stop);
     } else {
-        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF32, kF16>(a, gated, G, RB, UA, s, ev_start, ev_stop);
-        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF32, kF32>(a, gated, G, RB, UA, s, ev_start, ev_stop);
-        else launch_fused_kind<kF32, kQ4>(a, gated, G, RB, UA, s, ev_start, ev_stop);
+        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF32, kF16>(a, gated, G, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF32, kF32>(a, gated, G, UA, s, ev_start, ev_stop);
+        else launch_fused_kind<kF32, kQ4>(a, gated, G, UA, s, ev_start, ev_stop);
     }
     return hipGetLastError();
 }

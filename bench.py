@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=8)
     ap.add_argument("--cpu-layers", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time one library call per step instead of a replayed HIP graph")
     ap.add_argument("--profile-tokens", type=int, default=256)
     ap.add_argument("--n-cal", type=int, default=4096)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -215,16 +217,41 @@ def main():
     stream = torch.cuda.current_stream()
 
     # ---- sparse decode ---------------------------------------------------- #
+    # Eager: one library call per step (every kernel launched from the host).
     for k in range(W):
         spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=counts[0], ws=ws)
     torch.cuda.synchronize()
     log(f"[warmup] {W} steps done")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for k in range(K):
+        spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=counts[k], ws=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = ev0.elapsed_time(ev1) / K
+    log(f"[eager] {eager_ms:.3f} ms/step")
+
+    # Graph: the step captured once, replayed per token; the token is written
+    # into the captured input and the layer counts copied out after each replay.
+    xbuf = torch.empty(B, cfg.d, device=dev)
+    cbuf = torch.empty(nl, dtype=torch.int32, device=dev)
+    graph = None
+    if not args.eager:
+        graph = spffn.DecodeGraph(model, xbuf, h, layer_counts=cbuf, ws=ws)
+        for k in range(W):
+            xbuf.copy_(X[k % cfg.tokens])
+            graph.launch()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record(stream)
     for k in range(K):
-        spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=counts[k], ws=ws)
+        if graph is None:
+            spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=counts[k], ws=ws)
+        else:
+            xbuf.copy_(X[k % cfg.tokens])
+            graph.launch()
+            counts[k].copy_(cbuf)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -236,8 +263,9 @@ def main():
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
     tok_s = B * K / (ms * 1e-3)
     active = cnt.mean() / cfg.d_ffn
-    log(f"[sparse] {ms_step:.3f} ms/step  {tok_s:.1f} tok/s  {gbs:.0f} GB/s  "
-        f"active {100 * active:.2f}%  wall {wall:.2f}s")
+    log(f"[sparse] {'eager' if graph is None else 'graph'}: {ms_step:.3f} ms/step  "
+        f"{tok_s:.1f} tok/s  {gbs:.0f} GB/s  active {100 * active:.2f}%  wall {wall:.2f}s")
+    del graph
 
     # ---- the dominant kernel, timed live with HIP events ------------------- #
     # A second timed pass of the same steps records an event pair around each
@@ -271,17 +299,26 @@ def main():
     # ---- dense baseline on the same kernels -------------------------------- #
     dense_ms = None
     if args.dense_steps > 0:
+        dgraph = None if args.eager else spffn.DecodeGraph(model, xbuf, h, dense=True, ws=ws)
+
+        def dense_step(k):
+            if dgraph is None:
+                spffn.decode_step(model, X[k % cfg.tokens], h, dense=True, ws=ws)
+            else:
+                xbuf.copy_(X[k % cfg.tokens])
+                dgraph.launch()
         for k in range(2):
-            spffn.decode_step(model, X[k], h, dense=True, ws=ws)
+            dense_step(k)
         torch.cuda.synchronize()
         ev0.record(stream)
         for k in range(args.dense_steps):
-            spffn.decode_step(model, X[k % cfg.tokens], h, dense=True, ws=ws)
+            dense_step(k)
         ev1.record(stream)
         torch.cuda.synchronize()
         dense_ms = ev0.elapsed_time(ev1) / args.dense_steps
         dgbs = dense_step_bytes(layers, B) / (dense_ms * 1e-3) / 1e9
         log(f"[dense] {dense_ms:.3f} ms/step  {dgbs:.0f} GB/s")
+        del dgraph
 
     # ---- CPU oracle on a bounded sample ------------------------------------ #
     cpu = None
@@ -332,6 +369,8 @@ def main():
             "touched_bytes_per_step": int(bytes_step),
             "achieved_GBps": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "decode_loop": "eager" if args.eager else "hip_graph",
+            "eager_ms_per_step": round(eager_ms, 4),
             "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 4),
             "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         },

@@ -210,6 +210,27 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
                                int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
                                void *ws, size_t ws_bytes, void *stream);
 
+typedef struct spffn_graph spffn_graph; /* [host] opaque: a captured decode step */
+
+/* Capture one spffn_decode_step (same arguments, no trace) into a HIP graph
+ * for replay: a decode loop then issues one graph launch per token instead of
+ * one launch per kernel.  The capture runs on a private stream of the
+ * library's own and enqueues no device work; it records the pointers it is
+ * given, so every replay reads x, writes h and layer_counts and uses ws at
+ * those addresses, and the caller changes the input by writing into x between
+ * replays.  The buffers must stay allocated while the graph exists, and two
+ * replays in flight at once (or a replay and any other call using the same
+ * ws) race.  Errors as spffn_decode_step, plus SPFFN_E_HIP when the runtime
+ * cannot capture or instantiate.  *out is set only on SPFFN_OK. */
+spffn_status spffn_decode_graph_create(const spffn_model *model, const float *x, float *h,
+                                       int32_t B, int32_t flags, int32_t *layer_counts, void *ws,
+                                       size_t ws_bytes, spffn_graph **out);
+
+/* Enqueue one replay of the captured step on `stream` (hipStream_t). */
+spffn_status spffn_graph_launch(const spffn_graph *graph, void *stream);
+
+void spffn_graph_destroy(spffn_graph *graph);
+
 /* ---- load-time utilities ---------------------------------------------- */
 
 /* Activation profile over N tokens x [N, d] (N >= 1): counts[i] (device

@@ -156,6 +156,17 @@ def test_model_validation():
     ws = C.c_void_p(0x100000)
     assert lib.spffn_decode_step(m, x, x, 1, 4, None, None, ws, nb, None) == E_ARG  # bad flag
     assert lib.spffn_decode_step(m, x, x, 1, 0, None, None, ws, nb - 256, None) == E_WORKSPACE
+    # graph capture validates like decode_step before touching the runtime
+    g = C.c_void_p()
+    assert lib.spffn_decode_graph_create(m, x, x, 1, 0, None, ws, nb, None) == E_ARG
+    assert lib.spffn_decode_graph_create(m, x, x, 1, 4, None, ws, nb, C.byref(g)) == E_ARG
+    assert lib.spffn_decode_graph_create(m, x, x, 0, 0, None, ws, nb, C.byref(g)) == E_SHAPE
+    assert lib.spffn_decode_graph_create(m, x, x, 1, 0, None, ws, nb - 256,
+                                         C.byref(g)) == E_WORKSPACE
+    assert lib.spffn_decode_graph_create(None, x, x, 1, 0, None, ws, nb, C.byref(g)) == E_ARG
+    assert g.value is None
+    assert lib.spffn_graph_launch(None, None) == E_ARG
+    lib.spffn_graph_destroy(None)  # no-op
     lib.spffn_model_destroy(m)
     lib.spffn_layer_destroy(a)
     lib.spffn_layer_destroy(b)
