@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspffn.so")
-SOURCES = ["api.hip", "kernels_misc.hip", "kernels_gemv.hip", "kernels_ffn.hip", "kernels_b1.hip"]
+SOURCES = ["api.hip", "kernels_misc.hip", "kernels_gemv.hip", "kernels_ffn.hip", "kernels_b1.hip",
+           "kernels_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -65,9 +65,11 @@ WMat wmat(const void *p, int dtype, int rows, int cols) {
 }
 
 struct Ws {
-    float *n, *hid, *act, *part, *scale, *lst_a;
+    float *n, *hid, *act, *part, *scale, *lst_a, *w1p;
     uint8_t *mask, *uni;
     int32_t *idx, *count, *gcnt, *lst_i;
+    _Float16 *xhi, *xlo, *hhi, *hlo, *ahi, *alo;
+    int ld_act;
     int chunks;
 };
 
@@ -87,6 +89,14 @@ Ws carve(const Layer &L, int B, void *ws) {
     w.lst_i = reinterpret_cast<int32_t *>(base + lo.lst_i);
     w.lst_a = reinterpret_cast<float *>(base + lo.lst_a);
     w.part = reinterpret_cast<float *>(base + lo.part);
+    w.w1p = reinterpret_cast<float *>(base + lo.w1p);
+    w.xhi = reinterpret_cast<_Float16 *>(base + lo.xhi);
+    w.xlo = reinterpret_cast<_Float16 *>(base + lo.xlo);
+    w.hhi = reinterpret_cast<_Float16 *>(base + lo.hhi);
+    w.hlo = reinterpret_cast<_Float16 *>(base + lo.hlo);
+    w.ahi = reinterpret_cast<_Float16 *>(base + lo.ahi);
+    w.alo = reinterpret_cast<_Float16 *>(base + lo.alo);
+    w.ld_act = lo.ld_act;
     w.chunks = lo.chunks;
     return w;
 }
@@ -110,9 +120,10 @@ bool single(const Layer &L, int B) { return B == 1 && b1_fits(L); }
 // The FFN part of one layer for B tokens over (idx, count) or every neuron.
 // x is normalised by `scale` (device, per token) when scale != nullptr; the
 // output is written to y, plus resid when resid != nullptr.
+// split_ready: the batched path's fp16 split of x is already in w.xhi/xlo.
 spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
                      const int32_t *idx, const int32_t *count, const float *resid, float *y,
-                     const Ws &w, hipStream_t s) {
+                     const Ws &w, hipStream_t s, bool split_ready = false) {
     if (single(L, B)) {
         SPFFN_HIP(launch_up_b1(L, x, scale, idx, count, w.act, s), "gather up/gate launch");
         SPFFN_HIP(launch_down_b1(L, idx, count, w.act, w.part, w.chunks, s), "gather down launch");
@@ -120,6 +131,18 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
         return SPFFN_OK;
     }
     // the batched kernels take an already normalised input (scale unused)
+    if (mfma_fits(L, B)) {
+        if (!split_ready)
+            SPFFN_HIP(launch_split_act(x, B, L.desc.d, 0.0f, false, nullptr, w.xhi, w.xlo, s),
+                      "split launch");
+        SPFFN_HIP(launch_mfma_ffn(L, w.xhi, w.xlo, B, idx, count, w.ahi, w.alo, w.ld_act, w.part,
+                                  s),
+                  "batched gather launch");
+        SPFFN_HIP(launch_reduce_groups(w.part, mfma_down_chunks(), (int64_t)B * L.desc.d, resid,
+                                       y, s),
+                  "reduce launch");
+        return SPFFN_OK;
+    }
     SPFFN_HIP(launch_ffn_up(L, x, B, idx, count, w.act, s), "gather up/gate launch");
     SPFFN_HIP(launch_ffn_down(L, B, idx, count, w.act, w.part, w.chunks, s),
               "gather down launch");
@@ -131,7 +154,8 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
 // Predictor of B tokens.  normalize: x is the residual stream and is RMS
 // normalised first (decode); the RMS scale goes to w.scale.
 spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, float eps,
-                         float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s) {
+                         float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s,
+                         bool split_ready = false) {
     const spffn_layer_desc &D = L.desc;
     if (single(L, B)) {
         SPFFN_HIP(launch_w1_b1(L, x, eps, normalize, w.hid, w.scale, s), "predictor layer-1 launch");
@@ -139,6 +163,15 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
         SPFFN_HIP(launch_w2_b1(L, w.hid, logits, m, s), "predictor layer-2 launch");
         if (mask && uni)
             SPFFN_HIP(hipMemcpyAsync(uni, mask, D.d_ffn, hipMemcpyDeviceToDevice, s), "union copy");
+        return SPFFN_OK;
+    }
+    if (mfma_fits(L, B)) {
+        if (!split_ready)
+            SPFFN_HIP(launch_split_act(x, B, D.d, eps, normalize, w.n, w.xhi, w.xlo, s),
+                      "split launch");
+        SPFFN_HIP(launch_mfma_predict(L, w.xhi, w.xlo, B, w.w1p, w.hid, w.hhi, w.hlo, logits, mask,
+                                      uni, s),
+                  "batched predictor launch");
         return SPFFN_OK;
     }
     const float *xin = x;
@@ -190,8 +223,28 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
         lo.chunks = down_b1_chunks(L);
         if (fused_fits(L) && fused_chunks(L) > lo.chunks) lo.chunks = fused_chunks(L);
     }
+    if (B > 1 && mfma_fits(L, B) && mfma_down_chunks() > lo.chunks) lo.chunks = mfma_down_chunks();
     lo.part = off;
     off += up256((size_t)lo.chunks * B * D.d * 4);
+    // fp16 splits of the batched path (only when it applies)
+    const bool mf = B > 1 && mfma_fits(L, B);
+    lo.ld_act = (D.d_ffn + 7) / 8 * 8;
+    const size_t nx = mf ? (size_t)B * D.d * 2 : 0, nh = mf ? (size_t)B * D.r * 2 : 0;
+    const size_t na = mf ? (size_t)B * lo.ld_act * 2 : 0;
+    lo.xhi = off;
+    off += up256(nx);
+    lo.xlo = off;
+    off += up256(nx);
+    lo.hhi = off;
+    off += up256(nh);
+    lo.hlo = off;
+    off += up256(nh);
+    lo.ahi = off;
+    off += up256(na);
+    lo.alo = off;
+    off += up256(na);
+    lo.w1p = off;
+    off += up256(mf ? (size_t)mfma_w1_splits() * B * D.r * 4 : 0);
     lo.total = off;
     return lo;
 }
@@ -523,10 +576,17 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         const bool one = single(L, B);
         // single token: the predictor's first kernel computes the RMS scale and
         // every kernel normalises on the fly; batches normalise into w.n first
+        // (the matrix-core path also splits the normalised input into fp16 halves)
         const float *xin = one ? h : w.n;
-        if (!one) SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
+        const bool mf = !one && mfma_fits(L, B);
+        if (mf)
+            SPFFN_HIP(launch_split_act(h, B, d, model->eps, true, w.n, w.xhi, w.xlo, s),
+                      "rmsnorm launch");
+        else if (!one)
+            SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
         if (!dense) {
-            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s))) return st;
+            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf)))
+                return st;
             SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,
                                      layer_counts ? layer_counts + l : nullptr),
                       "compact launch");
@@ -543,7 +603,7 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         }
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
-        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s))) return st;
+        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s, mf))) return st;
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
         mask_off += F;

@@ -33,6 +33,8 @@ struct Layer {
 // Workspace carve-up for a batch of B tokens.
 struct WsLayout {
     size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, part, total;
+    size_t xhi, xlo, hhi, hlo, ahi, alo, w1p;  // fp16 splits and partials of the batched path
+    int ld_act;  // row pitch (elements) of ahi / alo
     int chunks;  // neuron chunks of the down projection (partial-sum slots)
 };
 
@@ -86,6 +88,19 @@ hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, cons
                         const int32_t *count, float *act, hipStream_t s);
 hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *count,
                           const float *act, float *part, int chunks, hipStream_t s);
+// Batched path on the matrix cores (fp16 weights, 2 <= B <= 16).
+bool mfma_fits(const Layer &L, int B);
+int mfma_down_chunks();
+int mfma_w1_splits();
+hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
+                            _Float16 *hi, _Float16 *lo, hipStream_t s);
+hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                               float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
+                               float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s);
+hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                           const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
+                           int ld_act, float *part, hipStream_t s);
+
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s);
 

@@ -1,0 +1,443 @@
+// Batched (2 <= B <= 16 tokens) kernels on the matrix cores, for fp16 weights.
+//
+// A batch of B tokens turns every matrix-vector product of the layer into a
+// product with B columns.  Each weight byte is then used B times, which at
+// B = 16 is more multiply-adds than the vector units finish in the time HBM
+// delivers the bytes, so the products run on v_mfma_f32_16x16x32_f16:
+//
+//   * the weights are the A operand (16 rows x 32 columns of K per
+//     instruction), loaded from HBM straight into registers -- a lane's 8
+//     halves are 16 contiguous bytes of one row;
+//   * the activations are the B operand, kept in fp32 precision by splitting
+//     each value into two halves, x = hi + lo with hi = fp16(x) and
+//     lo = fp16(x - hi) (the pair carries about 22 significant bits); for
+//     B <= 8 the hi and lo parts of the B tokens share one instruction
+//     (columns 0..7 and 8..15) and the two halves of the result are added,
+//     for B > 8 they take one instruction each into the same accumulator;
+//   * accumulation is fp32 throughout.
+//
+// Operand layouts of the instruction (wave64), checked on the device:
+//   A lane l: row l % 16, k = 8 (l / 16) + i;   B lane l: column l % 16,
+//   k = 8 (l / 16) + i;   D lane l: rows 4 (l / 16) + i, column l % 16.
+// The contraction order over k is free, so a lane may take S consecutive
+// packets of its row (16 S contiguous bytes) and feed them to S instructions
+// as long as the B operand uses the same k for the same lane.
+//
+// The down projection contracts over the gathered rows, which are not
+// contiguous in memory, so its workgroups stage 32 gathered rows x 512
+// columns in LDS and read the B operand out of LDS transposed; the
+// activations (split the same way) are the A operand, tokens as rows.
+#include "device.h"
+
+namespace spffn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(half8 a, half8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+// 16 bytes of activations (8 halves) from L2-resident memory.
+__device__ __forceinline__ half8 ld_half8(const _Float16 *p) {
+    return as_half8(*reinterpret_cast<const uint4 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// x [B, K] fp32 -> (optionally RMS-normalised) n, and its hi/lo fp16 split.
+// One block per token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void split_act_kernel(const float *__restrict__ x, int K,
+                                                        float eps, int normalize,
+                                                        float *__restrict__ n_out,
+                                                        _Float16 *__restrict__ hi,
+                                                        _Float16 *__restrict__ lo) {
+    __shared__ float red[4];
+    const int b = blockIdx.x;
+    const float *xb = x + (size_t)b * K;
+    float s = 1.0f;
+    if (normalize) {
+        float ss = 0.0f;
+        for (int k = threadIdx.x; k < K; k += blockDim.x) ss = fmaf(xb[k], xb[k], ss);
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        const float tot = red[0] + red[1] + red[2] + red[3];
+        s = 1.0f / sqrtf(tot / (float)K + eps);
+    }
+    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        const float v = xb[k] * s;
+        const _Float16 h = (_Float16)v;
+        const size_t o = (size_t)b * K + k;
+        if (n_out) n_out[o] = v;
+        hi[o] = h;
+        lo[o] = (_Float16)(v - (float)h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched GEMV on the matrix cores: for a tile of 16 rows (a dense range, or
+// entries j of an index list) and B tokens,
+//     Z[row, b] = sum_k W[row, k] x[b, k]
+// over the workgroup's K range (WV waves, each a contiguous quarter/eighth of
+// it; blockIdx.y picks the range when K is split across workgroups), reduced
+// over the waves in a fixed order, then one of three epilogues.
+// ---------------------------------------------------------------------------
+enum { kEpiPartial = 0, kEpiMask = 1, kEpiAct = 2 };
+
+struct BgArgs {
+    const _Float16 *wa;  // [rows, K] (gate for ReGLU, else the one matrix)
+    const _Float16 *wu;  // [rows, K] W_up for ReGLU
+    int K;
+    int rows;              // rows of the matrix
+    const int32_t *idx;    // gathered: row of list entry j; nullptr: dense
+    const int32_t *count;  // device count of the list (gathered only)
+    const _Float16 *xhi, *xlo;  // [B, K]
+    int B;
+    // epilogues
+    const float *bias;     // [rows] or nullptr (mask: b2; act: b_act)
+    float t;               // mask: logit threshold
+    float *part;           // partial: [gridDim.y, B, rows]
+    float *logits;         // mask: [B, rows] or nullptr
+    uint8_t *mask;         // mask: [B, rows] or nullptr
+    uint8_t *uni;          // mask: [rows] or nullptr
+    _Float16 *ahi, *alo;   // act: [B, ld_act], entry j of the list
+    int ld_act;
+};
+
+template <int WV, bool GATED, bool SPLIT2, int S, int EPI>
+__global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
+    __shared__ float red[WV][GATED ? 2 : 1][256];
+    __shared__ uint32_t s_any[16];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int m = lane & 15, q = lane >> 4;
+    const int n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
+    const int j0 = blockIdx.x * 16;
+    if (j0 >= n_items) return;  // whole block: the grid covers the largest list
+    const int j = j0 + m;
+    int row = j < n_items ? (a.idx ? a.idx[j] : j) : (a.idx ? a.idx[j0] : j0);
+    row = min(max(row, 0), a.rows - 1);
+
+    const int Kw = a.K / (WV * gridDim.y);
+    const int k0 = (blockIdx.y * WV + wv) * Kw;
+    const _Float16 *pa = a.wa + (size_t)row * a.K + k0 + 8 * S * q;
+    const _Float16 *pu = GATED ? a.wu + (size_t)row * a.K + k0 + 8 * S * q : nullptr;
+    // B operand source of this lane: token m (SPLIT2), or token m & 7 of the
+    // hi (m < 8) / lo (m >= 8) half
+    const int tok = SPLIT2 ? m : (m & 7);
+    const bool tv = tok < a.B;
+    const _Float16 *px = (SPLIT2 || m < 8 ? a.xhi : a.xlo) + (size_t)(tv ? tok : 0) * a.K + k0 +
+                         8 * S * q;
+    const _Float16 *pxl = a.xlo + (size_t)(tv ? tok : 0) * a.K + k0 + 8 * S * q;
+
+    f32x4 ca = {0.0f, 0.0f, 0.0f, 0.0f}, cu = {0.0f, 0.0f, 0.0f, 0.0f};
+    const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kb = 0; kb < Kw; kb += 32 * S) {
+        uint4 wa_[S], wu_[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            wa_[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x4_t *>(pa + kb + 8 * s)));
+            if constexpr (GATED)
+                wu_[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                             reinterpret_cast<const u32x4_t *>(pu + kb + 8 * s)));
+        }
+        half8 xb[S], xl[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            xb[s] = tv ? ld_half8(px + kb + 8 * s) : zero8;
+            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + kb + 8 * s) : zero8;
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            ca = mfma16x16x32(as_half8(wa_[s]), xb[s], ca);
+            if constexpr (SPLIT2) ca = mfma16x16x32(as_half8(wa_[s]), xl[s], ca);
+            if constexpr (GATED) {
+                cu = mfma16x16x32(as_half8(wu_[s]), xb[s], cu);
+                if constexpr (SPLIT2) cu = mfma16x16x32(as_half8(wu_[s]), xl[s], cu);
+            }
+        }
+    }
+
+    // fixed-order sum over the waves: red[w][.][r*16 + n]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        red[wv][0][(4 * q + i) * 16 + m] = ca[i];
+        if constexpr (GATED) red[wv][GATED ? 1 : 0][(4 * q + i) * 16 + m] = cu[i];
+    }
+    if (threadIdx.x < 16) s_any[threadIdx.x] = 0u;
+    __syncthreads();
+    // thread t < 256 owns tile entry (r = t / 16, n = t % 16); for B <= 8 the
+    // entries n < 8 add the lo half held in column n + 8
+    for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+        const int r = t >> 4, n = t & 15;
+        if (n >= a.B || (!SPLIT2 && n >= 8)) continue;
+        float za = 0.0f, zu = 0.0f;
+        for (int w = 0; w < WV; ++w) {
+            za += red[w][0][t];
+            if (!SPLIT2) za += red[w][0][t + 8];
+            if constexpr (GATED) {
+                zu += red[w][1][t];
+                if (!SPLIT2) zu += red[w][1][t + 8];
+            }
+        }
+        const int jj = j0 + r;
+        if (jj >= n_items) continue;
+        const int rr = a.idx ? a.idx[jj] : jj;
+        if constexpr (EPI == kEpiPartial) {
+            a.part[((size_t)blockIdx.y * a.B + n) * a.rows + rr] = za;
+        } else if constexpr (EPI == kEpiMask) {
+            const float l = za + (a.bias ? a.bias[rr] : 0.0f);
+            const bool mk = l > a.t;
+            if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
+            if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
+            if (mk) atomicOr(&s_any[r], 1u);  // LDS
+        } else {
+            float v = fmaxf(za + (a.bias ? a.bias[rr] : 0.0f), 0.0f);
+            if constexpr (GATED) v *= zu;
+            const _Float16 h = (_Float16)v;
+            a.ahi[(size_t)n * a.ld_act + jj] = h;
+            a.alo[(size_t)n * a.ld_act + jj] = (_Float16)(v - (float)h);
+        }
+    }
+    if constexpr (EPI == kEpiMask) {
+        __syncthreads();
+        if (threadIdx.x < 16 && a.uni && j0 + (int)threadIdx.x < n_items) {
+            const int jj = j0 + threadIdx.x;
+            a.uni[a.idx ? a.idx[jj] : jj] = (uint8_t)(s_any[threadIdx.x] != 0u);
+        }
+    }
+}
+
+// hid[b, i] = ReLU(sum over the K splits of part + b1[i]), fp32 and split.
+__global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict__ part, int KS,
+                                                        int B, int r, const float *__restrict__ b1,
+                                                        float *__restrict__ hid,
+                                                        _Float16 *__restrict__ hhi,
+                                                        _Float16 *__restrict__ hlo) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= B * r) return;
+    const int i = t % r;
+    float v = 0.0f;
+    for (int c = 0; c < KS; ++c) v += part[(size_t)c * B * r + t];
+    v = fmaxf(v + (b1 ? b1[i] : 0.0f), 0.0f);
+    hid[t] = v;
+    const _Float16 h = (_Float16)v;
+    hhi[t] = h;
+    hlo[t] = (_Float16)(v - (float)h);
+}
+
+// ---------------------------------------------------------------------------
+// Down projection: part[c, b, col] = sum over list entries j of chunk c of
+// act[b, j] * W_down_t[idx[j], col], for the block's 512 columns.  Chunk c is
+// entries [c*per, (c+1)*per) with per = the list length over the chunks,
+// rounded up to a multiple of 32 (from the device count, so every chunk has
+// work whatever the list length).  Per step the block stages
+// 32 gathered rows x 512 columns (fp16) in LDS; wave w then owns columns
+// w*128 .. w*128+127 (8 tiles of 16) and reads its B operands transposed.
+// ---------------------------------------------------------------------------
+constexpr int kDownCols = 512;
+constexpr int kDownPitch = kDownCols + 8;  // halves per staged row (16-byte aligned)
+
+struct BdArgs {
+    const _Float16 *wd;  // W_down_t [rows, d]
+    int d, rows;
+    const int32_t *idx, *count;  // list (nullptr idx: dense)
+    const _Float16 *ahi, *alo;   // [B, ld_act]
+    int ld_act, B;
+    float *part;  // [gridDim.y, B, d]
+};
+
+template <bool SPLIT2>
+__global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
+    __shared__ __align__(16) _Float16 tile[32 * kDownPitch];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int m = lane & 15, q = lane >> 4;
+    const int slice = blockIdx.x, c = blockIdx.y;
+    const int n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
+    const int per = ((n_items + gridDim.y - 1) / gridDim.y + 31) / 32 * 32;
+    const int j0 = min(n_items, c * per), j1 = min(n_items, j0 + per);
+    const int col0 = slice * kDownCols;
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // A operand source: token m (SPLIT2) or token m & 7 of hi (m < 8) / lo
+    const int tok = SPLIT2 ? m : (m & 7);
+    const bool tv = tok < a.B;
+    const _Float16 *pa = (SPLIT2 || m < 8 ? a.ahi : a.alo) + (size_t)(tv ? tok : 0) * a.ld_act;
+    const _Float16 *pal = a.alo + (size_t)(tv ? tok : 0) * a.ld_act;
+    const int NP = a.d / 8;  // packets per row
+
+    for (int kb = j0; kb < j1; kb += 32) {
+        // stage rows kb .. kb+31 (zeros past j1): 32 rows x 64 packets
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            const int rr = f >> 6, p = f & 63;
+            const int jj = kb + rr;
+            const bool ok = jj < j1 && (col0 / 8 + p) < NP;
+            int row = ok ? (a.idx ? a.idx[jj] : jj) : 0;
+            row = min(max(row, 0), a.rows - 1);
+            const uint4 w = __builtin_bit_cast(
+                uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                           a.wd + (size_t)row * a.d + col0 + 8 * min(p, NP - 1 - col0 / 8))));
+            v[u] = ok ? w : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();  // the previous step's reads of the tile are done
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            const int rr = f >> 6, p = f & 63;
+            *reinterpret_cast<uint4 *>(&tile[rr * kDownPitch + 8 * p]) = v[u];
+        }
+        __syncthreads();
+        // A: act of list entries kb + 8q .. +7 (zero past j1)
+        half8 av, avl;
+        const int ja = kb + 8 * q;
+        if (tv && ja + 8 <= j1) {
+            av = ld_half8(pa + ja);
+            if constexpr (SPLIT2) avl = ld_half8(pal + ja);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool ok = tv && ja + i < j1;
+                av[i] = ok ? pa[ja + i] : (_Float16)0;
+                if constexpr (SPLIT2) avl[i] = ok ? pal[ja + i] : (_Float16)0;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int cc = wv * 128 + t * 16 + m;  // column within the slice
+            half8 bv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bv[i] = tile[(8 * q + i) * kDownPitch + cc];
+            acc[t] = mfma16x16x32(av, bv, acc[t]);
+            if constexpr (SPLIT2) acc[t] = mfma16x16x32(avl, bv, acc[t]);
+        }
+    }
+
+    // D lane (m, q): tokens 4q + i, column m of the tile.  B <= 8: rows 8..15
+    // hold the lo half of tokens 0..7, held by lanes q + 2.
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int col = col0 + wv * 128 + t * 16 + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = acc[t][i];
+            if constexpr (!SPLIT2) v += __shfl_down(v, 32, 64);
+            const int b = 4 * q + i;
+            const bool mine = SPLIT2 ? true : q < 2;
+            if (mine && b < a.B && col < a.d) a.part[((size_t)c * a.B + b) * a.d + col] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+constexpr int kBgWaves = 4;
+constexpr int kBgS = 4;
+constexpr int kW1Splits = 8;  // K splits of predictor layer 1 (few rows, long K)
+constexpr int kBdChunks = 32;
+
+bool mfma_fits(const Layer &L, int B) {
+    const spffn_layer_desc &D = L.desc;
+    if (B < 2 || B > 16) return false;
+    if (D.w_dtype != SPFFN_F16 || D.p_dtype != SPFFN_F16) return false;
+    const int kstep = 32 * kBgS * kBgWaves;
+    return D.d % (kstep * kW1Splits) == 0 && D.r % kstep == 0 && D.d % kDownCols == 0;
+}
+
+int mfma_down_chunks() { return kBdChunks; }
+int mfma_w1_splits() { return kW1Splits; }
+
+hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
+                            _Float16 *hi, _Float16 *lo, hipStream_t s) {
+    split_act_kernel<<<B, 256, 0, s>>>(x, K, eps, normalize ? 1 : 0, n_out, hi, lo);
+    return hipGetLastError();
+}
+
+template <bool GATED, int EPI>
+static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
+    if (a.B > 8) bgemv_kernel<kBgWaves, GATED, true, kBgS, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    else bgemv_kernel<kBgWaves, GATED, false, kBgS, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+}
+
+hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                               float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
+                               float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    BgArgs a{};
+    a.wa = reinterpret_cast<const _Float16 *>(L.w1.data);
+    a.K = D.d;
+    a.rows = D.r;
+    a.xhi = xhi;
+    a.xlo = xlo;
+    a.B = B;
+    a.part = w1part;
+    launch_bg<false, kEpiPartial>(a, dim3((D.r + 15) / 16, kW1Splits), s);
+    w1_finish_kernel<<<(B * D.r + 255) / 256, 256, 0, s>>>(w1part, kW1Splits, B, D.r, D.p_b1, hid,
+                                                          hhi, hlo);
+    BgArgs b{};
+    b.wa = reinterpret_cast<const _Float16 *>(L.w2.data);
+    b.K = D.r;
+    b.rows = D.d_ffn;
+    b.xhi = hhi;
+    b.xlo = hlo;
+    b.B = B;
+    b.bias = D.p_b2;
+    b.t = L.t;
+    b.logits = logits;
+    b.mask = mask;
+    b.uni = uni;
+    launch_bg<false, kEpiMask>(b, dim3((D.d_ffn + 15) / 16, 1), s);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                           const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
+                           int ld_act, float *part, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    const bool gated = D.kind == SPFFN_REGLU;
+    BgArgs a{};
+    a.wa = reinterpret_cast<const _Float16 *>((gated ? L.gate : L.up).data);
+    a.wu = reinterpret_cast<const _Float16 *>(L.up.data);
+    a.K = D.d;
+    a.rows = D.d_ffn;
+    a.idx = idx;
+    a.count = count;
+    a.xhi = xhi;
+    a.xlo = xlo;
+    a.B = B;
+    a.bias = D.b_act;
+    a.ahi = ahi;
+    a.alo = alo;
+    a.ld_act = ld_act;
+    const dim3 grid((D.d_ffn + 15) / 16, 1);
+    if (gated) launch_bg<true, kEpiAct>(a, grid, s);
+    else launch_bg<false, kEpiAct>(a, grid, s);
+
+    BdArgs b{};
+    b.wd = reinterpret_cast<const _Float16 *>(L.down.data);
+    b.d = D.d;
+    b.rows = D.d_ffn;
+    b.idx = idx;
+    b.count = count;
+    b.ahi = ahi;
+    b.alo = alo;
+    b.ld_act = ld_act;
+    b.B = B;
+    b.part = part;
+    const dim3 gd(D.d / kDownCols, kBdChunks);
+    if (B > 8) bdown_kernel<true><<<gd, 256, 0, s>>>(b);
+    else bdown_kernel<false><<<gd, 256, 0, s>>>(b);
+    return hipGetLastError();
+}
+
+}  // namespace spffn
