@@ -19,9 +19,10 @@
 // Operand layouts of the instruction (wave64), checked on the device:
 //   A lane l: row l % 16, k = 8 (l / 16) + i;   B lane l: column l % 16,
 //   k = 8 (l / 16) + i;   D lane l: rows 4 (l / 16) + i, column l % 16.
-// The contraction order over k is free, so a lane may take S consecutive
-// packets of its row (16 S contiguous bytes) and feed them to S instructions
-// as long as the B operand uses the same k for the same lane.
+// In that layout a load instruction could give each row only 64 contiguous
+// bytes (four lanes), which HBM serves poorly, so the weights are loaded
+// row-contiguously (256 bytes of each of 4 rows per instruction) into a
+// wave-private LDS tile and read back in the A layout.
 //
 // The down projection contracts over the gathered rows, which are not
 // contiguous in memory, so its workgroups stage 32 gathered rows x 512
@@ -48,8 +49,12 @@ __device__ __forceinline__ half8 ld_half8(const _Float16 *p) {
 
 // ---------------------------------------------------------------------------
 // x [B, K] fp32 -> (optionally RMS-normalised) n, and its hi/lo fp16 split.
-// One block per token.
+// Block (b, c) writes columns [c K/C, (c+1) K/C) of token b; with
+// normalisation every block of a token first sums the token's squares in the
+// same fixed order, so all of them use the same scale.
 // ---------------------------------------------------------------------------
+constexpr int kSplitChunks = 8;
+
 __global__ __launch_bounds__(256) void split_act_kernel(const float *__restrict__ x, int K,
                                                         float eps, int normalize,
                                                         float *__restrict__ n_out,
@@ -61,14 +66,23 @@ __global__ __launch_bounds__(256) void split_act_kernel(const float *__restrict_
     float s = 1.0f;
     if (normalize) {
         float ss = 0.0f;
-        for (int k = threadIdx.x; k < K; k += blockDim.x) ss = fmaf(xb[k], xb[k], ss);
+        const float4 *x4 = reinterpret_cast<const float4 *>(xb);
+        for (int k = threadIdx.x; k < K / 4; k += blockDim.x) {
+            const float4 v = x4[k];
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+        }
         ss = wave_sum(ss);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
         __syncthreads();
         const float tot = red[0] + red[1] + red[2] + red[3];
         s = 1.0f / sqrtf(tot / (float)K + eps);
     }
-    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    const int per = K / gridDim.y;
+    const int c0 = blockIdx.y * per;
+    for (int k = c0 + threadIdx.x; k < c0 + per; k += blockDim.x) {
         const float v = xb[k] * s;
         const _Float16 h = (_Float16)v;
         const size_t o = (size_t)b * K + k;
@@ -108,65 +122,96 @@ struct BgArgs {
     int ld_act;
 };
 
-template <int WV, bool GATED, bool SPLIT2, int S, int EPI>
+template <int WV, bool GATED, bool SPLIT2, int EPI>
 __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
-    __shared__ float red[WV][GATED ? 2 : 1][256];
+    constexpr int NM = GATED ? 2 : 1;
+    // per wave: the current 16 rows x 128 columns of each matrix (16 chunks of
+    // 16 B per row, chunk c of row r at slot c ^ r); reused for the
+    // cross-wave sums once the K loop is done
+    __shared__ uint4 stg[WV][NM][16][16];
     __shared__ uint32_t s_any[16];
+    float(*red)[NM][256] = reinterpret_cast<float(*)[NM][256]>(&stg[0][0][0][0]);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, q = lane >> 4;
     const int n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
     const int j0 = blockIdx.x * 16;
     if (j0 >= n_items) return;  // whole block: the grid covers the largest list
-    const int j = j0 + m;
-    int row = j < n_items ? (a.idx ? a.idx[j] : j) : (a.idx ? a.idx[j0] : j0);
-    row = min(max(row, 0), a.rows - 1);
 
     const int Kw = a.K / (WV * gridDim.y);
     const int k0 = (blockIdx.y * WV + wv) * Kw;
-    const _Float16 *pa = a.wa + (size_t)row * a.K + k0 + 8 * S * q;
-    const _Float16 *pu = GATED ? a.wu + (size_t)row * a.K + k0 + 8 * S * q : nullptr;
+    // Weight loads are row-contiguous: load g (of 4) gives lane l chunk l & 15
+    // (8 columns) of tile row 4g + (l >> 4), i.e. 256 contiguous bytes of each
+    // of 4 rows per instruction.  Through LDS each lane then picks up the
+    // chunks of the A layout (row m, columns 32s + 8q).
+    const _Float16 *pa[4], *pu[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int jr = j0 + 4 * g + (lane >> 4);
+        int rr = jr < n_items ? (a.idx ? a.idx[jr] : jr) : (a.idx ? a.idx[j0] : j0);
+        rr = min(max(rr, 0), a.rows - 1);
+        pa[g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
+        pu[g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
+    }
     // B operand source of this lane: token m (SPLIT2), or token m & 7 of the
-    // hi (m < 8) / lo (m >= 8) half
+    // hi (m < 8) / lo (m >= 8) half; columns 32s + 8q of each 128
     const int tok = SPLIT2 ? m : (m & 7);
     const bool tv = tok < a.B;
     const _Float16 *px = (SPLIT2 || m < 8 ? a.xhi : a.xlo) + (size_t)(tv ? tok : 0) * a.K + k0 +
-                         8 * S * q;
-    const _Float16 *pxl = a.xlo + (size_t)(tv ? tok : 0) * a.K + k0 + 8 * S * q;
+                         8 * q;
+    const _Float16 *pxl = a.xlo + (size_t)(tv ? tok : 0) * a.K + k0 + 8 * q;
 
     f32x4 ca = {0.0f, 0.0f, 0.0f, 0.0f}, cu = {0.0f, 0.0f, 0.0f, 0.0f};
     const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int kb = 0; kb < Kw; kb += 32 * S) {
-        uint4 wa_[S], wu_[S];
+    for (int kb = 0; kb < Kw; kb += 128) {
+        uint4 ga[4], gu[4];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            wa_[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                         reinterpret_cast<const u32x4_t *>(pa + kb + 8 * s)));
+        for (int g = 0; g < 4; ++g) {
+            ga[g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4_t *>(pa[g] + kb)));
             if constexpr (GATED)
-                wu_[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                             reinterpret_cast<const u32x4_t *>(pu + kb + 8 * s)));
+                gu[g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4_t *>(pu[g] + kb)));
         }
-        half8 xb[S], xl[S];
+        half8 xb[4], xl[4];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            xb[s] = tv ? ld_half8(px + kb + 8 * s) : zero8;
-            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + kb + 8 * s) : zero8;
+        for (int s = 0; s < 4; ++s) {
+            xb[s] = tv ? ld_half8(px + kb + 32 * s) : zero8;
+            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + kb + 32 * s) : zero8;
         }
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            ca = mfma16x16x32(as_half8(wa_[s]), xb[s], ca);
-            if constexpr (SPLIT2) ca = mfma16x16x32(as_half8(wa_[s]), xl[s], ca);
+        for (int g = 0; g < 4; ++g) {
+            const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
+            stg[wv][0][r][c] = ga[g];
+            if constexpr (GATED) stg[wv][NM - 1][r][c] = gu[g];
+        }
+        // the wave's own LDS writes are complete before any lane reads them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = (4 * s + q) ^ m;
+            const half8 wa_ = as_half8(stg[wv][0][m][c]);
+            ca = mfma16x16x32(wa_, xb[s], ca);
+            if constexpr (SPLIT2) ca = mfma16x16x32(wa_, xl[s], ca);
             if constexpr (GATED) {
-                cu = mfma16x16x32(as_half8(wu_[s]), xb[s], cu);
-                if constexpr (SPLIT2) cu = mfma16x16x32(as_half8(wu_[s]), xl[s], cu);
+                const half8 wu_ = as_half8(stg[wv][NM - 1][m][c]);
+                cu = mfma16x16x32(wu_, xb[s], cu);
+                if constexpr (SPLIT2) cu = mfma16x16x32(wu_, xl[s], cu);
             }
         }
+        // and all reads are done before the next step overwrites the slots
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    __syncthreads();  // every wave is done with its slots before they hold sums
 
     // fixed-order sum over the waves: red[w][.][r*16 + n]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         red[wv][0][(4 * q + i) * 16 + m] = ca[i];
-        if constexpr (GATED) red[wv][GATED ? 1 : 0][(4 * q + i) * 16 + m] = cu[i];
+        if constexpr (GATED) red[wv][NM - 1][(4 * q + i) * 16 + m] = cu[i];
     }
     if (threadIdx.x < 16) s_any[threadIdx.x] = 0u;
     __syncthreads();
@@ -180,8 +225,8 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             za += red[w][0][t];
             if (!SPLIT2) za += red[w][0][t + 8];
             if constexpr (GATED) {
-                zu += red[w][1][t];
-                if (!SPLIT2) zu += red[w][1][t + 8];
+                zu += red[w][NM - 1][t];
+                if (!SPLIT2) zu += red[w][NM - 1][t + 8];
             }
         }
         const int jj = j0 + r;
@@ -271,32 +316,40 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
     const bool tv = tok < a.B;
     const _Float16 *pa = (SPLIT2 || m < 8 ? a.ahi : a.alo) + (size_t)(tv ? tok : 0) * a.ld_act;
     const _Float16 *pal = a.alo + (size_t)(tv ? tok : 0) * a.ld_act;
-    const int NP = a.d / 8;  // packets per row
-
-    for (int kb = j0; kb < j1; kb += 32) {
-        // stage rows kb .. kb+31 (zeros past j1): 32 rows x 64 packets
-        uint4 v[8];
+    // Thread t stages packet p = t & 63 of step rows (t >> 6) + 4u, u < 8.
+    // Software pipeline: the next step's row indices and weights are in
+    // flight while the current step's tile is multiplied.
+    const int p = threadIdx.x & 63, r0 = threadIdx.x >> 6;
+    auto rows_of = [&](int kb, int (&rv)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int f = threadIdx.x + 256 * u;
-            const int rr = f >> 6, p = f & 63;
-            const int jj = kb + rr;
-            const bool ok = jj < j1 && (col0 / 8 + p) < NP;
-            int row = ok ? (a.idx ? a.idx[jj] : jj) : 0;
-            row = min(max(row, 0), a.rows - 1);
+            const int jj = kb + r0 + 4 * u;
+            int row = jj < j1 ? (a.idx ? a.idx[jj] : jj) : -1;
+            rv[u] = row < 0 ? -1 : min(row, a.rows - 1);
+        }
+    };
+    auto load_w = [&](const int (&rv)[8], uint4 (&vv)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
             const uint4 w = __builtin_bit_cast(
                 uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
-                           a.wd + (size_t)row * a.d + col0 + 8 * min(p, NP - 1 - col0 / 8))));
-            v[u] = ok ? w : make_uint4(0, 0, 0, 0);
+                           a.wd + (size_t)(rv[u] < 0 ? 0 : rv[u]) * a.d + col0 + 8 * p)));
+            vv[u] = rv[u] >= 0 ? w : make_uint4(0, 0, 0, 0);
         }
+    };
+    int rowv[8];
+    uint4 v[8];
+    rows_of(j0, rowv);
+    load_w(rowv, v);
+    for (int kb = j0; kb < j1; kb += 32) {
+        int nrow[8];
+        rows_of(kb + 32, nrow);
         __syncthreads();  // the previous step's reads of the tile are done
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int f = threadIdx.x + 256 * u;
-            const int rr = f >> 6, p = f & 63;
-            *reinterpret_cast<uint4 *>(&tile[rr * kDownPitch + 8 * p]) = v[u];
-        }
+        for (int u = 0; u < 8; ++u)
+            *reinterpret_cast<uint4 *>(&tile[(r0 + 4 * u) * kDownPitch + 8 * p]) = v[u];
         __syncthreads();
+        load_w(nrow, v);
         // A: act of list entries kb + 8q .. +7 (zero past j1)
         half8 av, avl;
         const int ja = kb + 8 * q;
@@ -342,7 +395,6 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
 // dispatch
 // ---------------------------------------------------------------------------
 constexpr int kBgWaves = 4;
-constexpr int kBgS = 4;
 constexpr int kW1Splits = 8;  // K splits of predictor layer 1 (few rows, long K)
 constexpr int kBdChunks = 32;
 
@@ -350,7 +402,7 @@ bool mfma_fits(const Layer &L, int B) {
     const spffn_layer_desc &D = L.desc;
     if (B < 2 || B > 16) return false;
     if (D.w_dtype != SPFFN_F16 || D.p_dtype != SPFFN_F16) return false;
-    const int kstep = 32 * kBgS * kBgWaves;
+    const int kstep = 128 * kBgWaves;  // each wave's K range is whole 128-column steps
     return D.d % (kstep * kW1Splits) == 0 && D.r % kstep == 0 && D.d % kDownCols == 0;
 }
 
@@ -359,14 +411,16 @@ int mfma_w1_splits() { return kW1Splits; }
 
 hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
                             _Float16 *hi, _Float16 *lo, hipStream_t s) {
-    split_act_kernel<<<B, 256, 0, s>>>(x, K, eps, normalize ? 1 : 0, n_out, hi, lo);
+    // K is a multiple of 4096 on this path, so the chunks are whole float4s
+    split_act_kernel<<<dim3(B, kSplitChunks), 256, 0, s>>>(x, K, eps, normalize ? 1 : 0, n_out,
+                                                           hi, lo);
     return hipGetLastError();
 }
 
 template <bool GATED, int EPI>
 static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
-    if (a.B > 8) bgemv_kernel<kBgWaves, GATED, true, kBgS, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
-    else bgemv_kernel<kBgWaves, GATED, false, kBgS, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    if (a.B > 8) bgemv_kernel<kBgWaves, GATED, true, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    else bgemv_kernel<kBgWaves, GATED, false, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
 }
 
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
