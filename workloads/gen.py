@@ -28,7 +28,7 @@ from .configs import Config
 
 # tensor tags mixed into the per-tensor seed
 TAG_RANK, TAG_GATE, TAG_UP, TAG_DOWN, TAG_W1, TAG_CAL = 1, 2, 3, 4, 5, 6
-TAG_Q4_CODES, TAG_Q4_SCALES = 7, 8
+TAG_Q4_CODES, TAG_Q4_SCALES, TAG_SHIFT = 7, 8, 9
 TAG_TOKENS, TAG_PROFILE = 20, 21
 
 Q4_0_BLOCK, Q4_0_BYTES = 32, 18
@@ -148,7 +148,14 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
     b2 = sol[r].float()
     if cfg.p_dtype == "f16":
         w2 = w2.half()
-    lcal = hcal @ w2.float().t() + b2                # [n_cal, F]
+    # the per-neuron shift is taken on held-out tokens: the fit's own tokens have
+    # less residual variance than new ones, which would bias every rate upward
+    del hcal
+    xq = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_SHIFT), device=dev)
+    hq = torch.relu(xq @ w1.float().t() + b1)
+    del xq
+    lcal = hq @ w2.float().t() + b2                  # [n_cal, F]
+    del hq
     srt = torch.sort(lcal, dim=0, descending=True).values
     del lcal
     k = torch.from_numpy(np.clip(np.rint(p * n_cal), 0, n_cal).astype(np.int64)).to(dev)
