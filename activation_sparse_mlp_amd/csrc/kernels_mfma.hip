@@ -122,19 +122,21 @@ struct BgArgs {
     int ld_act;
 };
 
-template <int WV, bool GATED, bool SPLIT2, int EPI>
+template <int WV, int T, bool GATED, bool SPLIT2, int EPI>
 __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     constexpr int NM = GATED ? 2 : 1;
-    // per wave: the current 16 rows x 128 columns of each matrix (16 chunks of
-    // 16 B per row, chunk c of row r at slot c ^ r); reused for the
-    // cross-wave sums once the K loop is done
-    __shared__ uint4 stg[WV][NM][16][16];
-    __shared__ uint32_t s_any[16];
-    float(*red)[NM][256] = reinterpret_cast<float(*)[NM][256]>(&stg[0][0][0][0]);
+    // T tiles of 16 rows per workgroup; every wave runs all T tiles over its K
+    // range, so each activation operand it loads feeds T tiles.
+    // Per wave: the current 16 rows x 128 columns of each tile and matrix (16
+    // chunks of 16 B per row, chunk c of row r at slot c ^ r); reused for the
+    // cross-wave sums once the K loop is done.
+    __shared__ uint4 stg[WV][NM][T][16][16];
+    __shared__ uint32_t s_any[16 * T];
+    float(*red)[NM][T][256] = reinterpret_cast<float(*)[NM][T][256]>(&stg[0][0][0][0][0]);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, q = lane >> 4;
     const int n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
-    const int j0 = blockIdx.x * 16;
+    const int j0 = blockIdx.x * 16 * T;
     if (j0 >= n_items) return;  // whole block: the grid covers the largest list
 
     const int Kw = a.K / (WV * gridDim.y);
@@ -143,15 +145,17 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     // (8 columns) of tile row 4g + (l >> 4), i.e. 256 contiguous bytes of each
     // of 4 rows per instruction.  Through LDS each lane then picks up the
     // chunks of the A layout (row m, columns 32s + 8q).
-    const _Float16 *pa[4], *pu[4];
+    const _Float16 *pa[T][4], *pu[T][4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int jr = j0 + 4 * g + (lane >> 4);
-        int rr = jr < n_items ? (a.idx ? a.idx[jr] : jr) : (a.idx ? a.idx[j0] : j0);
-        rr = min(max(rr, 0), a.rows - 1);
-        pa[g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
-        pu[g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int jr = j0 + 16 * t + 4 * g + (lane >> 4);
+            int rr = jr < n_items ? (a.idx ? a.idx[jr] : jr) : (a.idx ? a.idx[j0] : j0);
+            rr = min(max(rr, 0), a.rows - 1);
+            pa[t][g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
+            pu[t][g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
+        }
     // B operand source of this lane: token m (SPLIT2), or token m & 7 of the
     // hi (m < 8) / lo (m >= 8) half; columns 32s + 8q of each 128
     const int tok = SPLIT2 ? m : (m & 7);
@@ -160,18 +164,22 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                          8 * q;
     const _Float16 *pxl = a.xlo + (size_t)(tv ? tok : 0) * a.K + k0 + 8 * q;
 
-    f32x4 ca = {0.0f, 0.0f, 0.0f, 0.0f}, cu = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 ca[T], cu[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) ca[t] = cu[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int kb = 0; kb < Kw; kb += 128) {
-        uint4 ga[4], gu[4];
+        uint4 ga[T][4], gu[T][4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            ga[g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4_t *>(pa[g] + kb)));
-            if constexpr (GATED)
-                gu[g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4_t *>(pu[g] + kb)));
-        }
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                ga[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                               reinterpret_cast<const u32x4_t *>(pa[t][g] + kb)));
+                if constexpr (GATED)
+                    gu[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                   reinterpret_cast<const u32x4_t *>(pu[t][g] + kb)));
+            }
         half8 xb[4], xl[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -179,27 +187,31 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + kb + 32 * s) : zero8;
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
-            stg[wv][0][r][c] = ga[g];
-            if constexpr (GATED) stg[wv][NM - 1][r][c] = gu[g];
-        }
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
+                stg[wv][0][t][r][c] = ga[t][g];
+                if constexpr (GATED) stg[wv][NM - 1][t][r][c] = gu[t][g];
+            }
         // the wave's own LDS writes are complete before any lane reads them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c = (4 * s + q) ^ m;
-            const half8 wa_ = as_half8(stg[wv][0][m][c]);
-            ca = mfma16x16x32(wa_, xb[s], ca);
-            if constexpr (SPLIT2) ca = mfma16x16x32(wa_, xl[s], ca);
-            if constexpr (GATED) {
-                const half8 wu_ = as_half8(stg[wv][NM - 1][m][c]);
-                cu = mfma16x16x32(wu_, xb[s], cu);
-                if constexpr (SPLIT2) cu = mfma16x16x32(wu_, xl[s], cu);
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int c = (4 * s + q) ^ m;
+                const half8 wa_ = as_half8(stg[wv][0][t][m][c]);
+                ca[t] = mfma16x16x32(wa_, xb[s], ca[t]);
+                if constexpr (SPLIT2) ca[t] = mfma16x16x32(wa_, xl[s], ca[t]);
+                if constexpr (GATED) {
+                    const half8 wu_ = as_half8(stg[wv][NM - 1][t][m][c]);
+                    cu[t] = mfma16x16x32(wu_, xb[s], cu[t]);
+                    if constexpr (SPLIT2) cu[t] = mfma16x16x32(wu_, xl[s], cu[t]);
+                }
             }
-        }
         // and all reads are done before the next step overwrites the slots
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -207,29 +219,31 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     }
     __syncthreads();  // every wave is done with its slots before they hold sums
 
-    // fixed-order sum over the waves: red[w][.][r*16 + n]
+    // fixed-order sum over the waves: red[w][.][t][r*16 + n]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        red[wv][0][(4 * q + i) * 16 + m] = ca[i];
-        if constexpr (GATED) red[wv][NM - 1][(4 * q + i) * 16 + m] = cu[i];
-    }
-    if (threadIdx.x < 16) s_any[threadIdx.x] = 0u;
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            red[wv][0][t][(4 * q + i) * 16 + m] = ca[t][i];
+            if constexpr (GATED) red[wv][NM - 1][t][(4 * q + i) * 16 + m] = cu[t][i];
+        }
+    if (threadIdx.x < 16 * T) s_any[threadIdx.x] = 0u;
     __syncthreads();
-    // thread t < 256 owns tile entry (r = t / 16, n = t % 16); for B <= 8 the
-    // entries n < 8 add the lo half held in column n + 8
-    for (int t = threadIdx.x; t < 256; t += blockDim.x) {
-        const int r = t >> 4, n = t & 15;
+    // entry e < 256 T is (tile t = e / 256, row r = e / 16 % 16, column n =
+    // e % 16); for B <= 8 the entries n < 8 add the lo half held in column n + 8
+    for (int e = threadIdx.x; e < 256 * T; e += blockDim.x) {
+        const int t = e >> 8, te = e & 255, r = te >> 4, n = te & 15;
         if (n >= a.B || (!SPLIT2 && n >= 8)) continue;
         float za = 0.0f, zu = 0.0f;
         for (int w = 0; w < WV; ++w) {
-            za += red[w][0][t];
-            if (!SPLIT2) za += red[w][0][t + 8];
+            za += red[w][0][t][te];
+            if (!SPLIT2) za += red[w][0][t][te + 8];
             if constexpr (GATED) {
-                zu += red[w][NM - 1][t];
-                if (!SPLIT2) zu += red[w][NM - 1][t + 8];
+                zu += red[w][NM - 1][t][te];
+                if (!SPLIT2) zu += red[w][NM - 1][t][te + 8];
             }
         }
-        const int jj = j0 + r;
+        const int jj = j0 + 16 * t + r;
         if (jj >= n_items) continue;
         const int rr = a.idx ? a.idx[jj] : jj;
         if constexpr (EPI == kEpiPartial) {
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             const bool mk = l > a.t;
             if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
             if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
-            if (mk) atomicOr(&s_any[r], 1u);  // LDS
+            if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
         } else {
             float v = fmaxf(za + (a.bias ? a.bias[rr] : 0.0f), 0.0f);
             if constexpr (GATED) v *= zu;
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     }
     if constexpr (EPI == kEpiMask) {
         __syncthreads();
-        if (threadIdx.x < 16 && a.uni && j0 + (int)threadIdx.x < n_items) {
+        if ((int)threadIdx.x < 16 * T && a.uni && j0 + (int)threadIdx.x < n_items) {
             const int jj = j0 + threadIdx.x;
             a.uni[a.idx ? a.idx[jj] : jj] = (uint8_t)(s_any[threadIdx.x] != 0u);
         }
@@ -417,10 +431,17 @@ hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normal
     return hipGetLastError();
 }
 
+// Two 16-row tiles per workgroup when B > 8 (the activation operand then
+// costs as many bytes as the weights, so sharing it halves that traffic);
+// grid.x counts 16-row tiles and is rounded to the workgroup's tiles here.
 template <bool GATED, int EPI>
 static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
-    if (a.B > 8) bgemv_kernel<kBgWaves, GATED, true, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
-    else bgemv_kernel<kBgWaves, GATED, false, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    if (a.B > 8) {
+        grid.x = (grid.x + 1) / 2;
+        bgemv_kernel<kBgWaves, 2, GATED, true, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    } else {
+        bgemv_kernel<kBgWaves, 1, GATED, false, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+    }
 }
 
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
