@@ -130,6 +130,15 @@ def measured_traffic(workload, batch):
     return None
 
 
+def batched_ffn_bytes(L, u, B):
+    """Algorithmic bytes of the batched FFN kernels of one layer (the event
+    pair brackets them when B > 1): the u listed rows of every FFN matrix, their
+    biases and index entries, the tokens' inputs and the residual in/out."""
+    row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
+    n_mat = 3 if L.kind == "reglu" else 2
+    return int(u) * (n_mat * row + 4 + 4) + B * 3 * L.d * 4
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime (the bench's own timing)."""
 
@@ -269,8 +278,9 @@ def main():
 
     # ---- the dominant kernel, timed live with HIP events ------------------- #
     # A second timed pass of the same steps records an event pair around each
-    # layer's largest kernel (the predictor layer-2 + gate/up gather kernel at
-    # batch 1); the headline pass above carries no per-kernel events.
+    # layer's largest kernel: the predictor layer-2 + gate/up gather kernel at
+    # batch 1 (every workload here takes the fused single-token path), the
+    # batched FFN kernels otherwise.  The headline pass carries no events.
     KE = max(1, min(K, 16))
     ev = HipEvents(2 * nl * KE)
     torch.cuda.synchronize()
@@ -285,11 +295,14 @@ def main():
     for k in range(KE):
         for l in range(nl):
             k_ms.append(ev.elapsed_ms(k * 2 * nl + 2 * l, k * 2 * nl + 2 * l + 1))
-            k_bytes.append(dominant_kernel_bytes(layers[l], kcnt[k, l], B))
+            k_bytes.append(dominant_kernel_bytes(layers[l], kcnt[k, l], B) if B == 1
+                           else batched_ffn_bytes(layers[l], kcnt[k, l], B))
     ev.close()
     kern_us = 1e3 * float(np.mean(k_ms))
     kern_gbs = float(np.mean(k_bytes)) / (kern_us * 1e-6) / 1e9
-    log(f"[kernel] predictor-2 + gather: {kern_us:.2f} us/launch  {kern_gbs:.0f} GB/s "
+    kern_name = ("predictor layer-2 + threshold + gate/up gather (one launch per layer)"
+                 if B == 1 else "batched FFN: gate/up gather, down projection, reduce (per layer)")
+    log(f"[kernel] {kern_name}: {kern_us:.2f} us/launch  {kern_gbs:.0f} GB/s "
         f"({len(k_ms)} launches)")
 
     traffic = measured_traffic(cfg.name, B) if nl == cfg.layers else None
@@ -376,7 +389,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "predictor layer-2 + threshold + gate/up gather (one launch per layer)",
+            "kernel": kern_name,
             "achieved": round(kern_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

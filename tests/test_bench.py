@@ -49,6 +49,11 @@ def test_dominant_kernel_bytes_by_hand():
         32 * 13 + 2 * (32 + 4 + 8) + (4 + 8) * 4
 
 
+def test_batched_ffn_bytes_by_hand():
+    # 7 listed rows of 3 fp16 matrices + bias + index; B=4 tokens: input, residual in/out
+    assert bench.batched_ffn_bytes(_layer(), 7, 4) == 7 * (3 * 16 + 8) + 4 * 3 * 8 * 4
+
+
 def test_dense_step_bytes_by_hand():
     assert bench.dense_step_bytes([_layer()], 1) == 32 * (3 * 16 + 4) + 2 * 8 * 4
 
