@@ -1,13 +1,18 @@
-// Single-token (batch 1) kernels of the decode path, built for latency on
-// gfx950: every wave issues its weight loads before the block stages the
-// activation vector, so the 128-bit streaming loads overlap the staging and
-// the normalisation; row pointers never wait on LDS.
+// Single-token (batch 1) kernels, built for latency on gfx950: every wave
+// issues its weight loads before anything that waits (LDS staging, the
+// normalisation, barriers), so the 128-bit streaming loads overlap them.
 //
-//   w1_b1      hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps) or 1
-//   w2_b1      logit = W2 . hid + b2, mask = logit > t
-//   up_b1      act_j = max(z, 0) [* u], z = (W_act[i] . h) * s + b_i, i = idx[j]
-//   down_b1    part[c, slice] = sum over run c of act_j * W_down_t[i, slice]
-//   reduce     y = sum_c part[c] (+ h)
+// Decode step, per layer (four kernels):
+//   w1_b1        hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps)
+//   pred2_up_b1  logit = W2 . hid + b2, mask = logit > t, and for the active
+//                rows of each 8-row group act = max(z, 0) [* u] with
+//                z = (W_act[i] . h) * s + b_i, listed per group
+//   down_list_b1 part[c, slice] = sum over the lists of chunk c of
+//                act * W_down_t[i, slice]
+//   reduce_groups h = h + sum_c part[c]
+// Single calls (spffn_predict / spffn_forward at one token): w1_b1, w2_b1
+// (logits and mask), up_b1 (activations of an index list), down_b1 (partials
+// over contiguous runs of the list), reduce_groups.
 // (s is the RMS scale; multiplying the dot product by it equals normalising
 // the vector first, up to rounding.)
 #include <hip/hip_ext.h>

@@ -104,12 +104,25 @@ def dominant_kernel_bytes(L, u, B):
             + B * (L.r + L.d) * 4)
 
 
-def kernel_source_hash():
+def code_only(text):
+    """C++ source with comments and whitespace removed: what the hash covers,
+    so that editing a comment does not invalidate the stored counters."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
+def kernel_source_hash(read=None):
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel)) as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_only(text).encode())
     return h.hexdigest()
 
 

@@ -71,3 +71,11 @@ def test_traffic_record_lookup(tmp_path, monkeypatch):
     assert bench.measured_traffic("w2", 1) is None       # kernel changed since
     monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(tmp_path / "missing.md"))
     assert bench.measured_traffic("w", 1) is None
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {  // add one\n  return x + 1; /* done */ }\n"
+    b = "int f(int x){return x+1;}"
+    c = "int f(int x){return x+2;}"
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(b) != bench.code_only(c)
