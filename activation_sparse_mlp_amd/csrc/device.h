@@ -47,6 +47,22 @@ __device__ __forceinline__ float packet_scale(const WMat &w, size_t row, int col
         return 1.0f;
 }
 
+// Byte n (0..3) of a 32-bit word as a float, written so that it compiles to
+// one v_cvt_f32_ubyte<n> (4-bit codes are widened a byte at a time).
+__device__ __forceinline__ float byte_to_float(uint32_t w, int n) {
+    typedef unsigned char uchar4v __attribute__((ext_vector_type(4)));
+    const uchar4v b = __builtin_bit_cast(uchar4v, w);
+    return (float)b[n];
+}
+
+// w & mask as one v_and_b32 the compiler cannot split into per-byte bit-field
+// extracts, so that each byte is then widened by a single v_cvt_f32_ubyte<n>.
+__device__ __forceinline__ uint32_t and_word(uint32_t w, uint32_t mask) {
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(mask), "v"(w));
+    return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -134,29 +150,40 @@ __device__ __forceinline__ void packet_dot(const uint4 raw, float scale, const f
     } else {
         // 4-bit block: word m holds codes 4m..4m+3 in its low nibbles (group m)
         // and codes 16+4m..16+4m+3 in its high nibbles (group 4+m).
+        // low nibbles as bytes (q), high nibbles kept in place (16 q): both are
+        // exact in fp32, and the high sum is scaled by 1/16 exactly at the end
         const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
         float q[32];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
-            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lo = and_word(words[m], 0x0F0F0F0Fu);
+            const uint32_t hi = and_word(words[m], 0xF0F0F0F0u);
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
-                q[4 * m + n] = (float)((lo >> (8 * n)) & 0xFFu);
-                q[16 + 4 * m + n] = (float)((hi >> (8 * n)) & 0xFFu);
+                q[4 * m + n] = byte_to_float(lo, n);
+                q[16 + 4 * m + n] = byte_to_float(hi, n);
             }
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            float sq = 0.0f;
+            float sl = 0.0f, sh = 0.0f;
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
+            for (int g = 0; g < 4; ++g) {
                 const float4 v = lds4(xl + b * XS, NP, g, p);
-                sq = fmaf(q[4 * g + 0], v.x, sq);
-                sq = fmaf(q[4 * g + 1], v.y, sq);
-                sq = fmaf(q[4 * g + 2], v.z, sq);
-                sq = fmaf(q[4 * g + 3], v.w, sq);
+                sl = fmaf(q[4 * g + 0], v.x, sl);
+                sl = fmaf(q[4 * g + 1], v.y, sl);
+                sl = fmaf(q[4 * g + 2], v.z, sl);
+                sl = fmaf(q[4 * g + 3], v.w, sl);
             }
+#pragma unroll
+            for (int g = 4; g < 8; ++g) {
+                const float4 v = lds4(xl + b * XS, NP, g, p);
+                sh = fmaf(q[4 * g + 0], v.x, sh);
+                sh = fmaf(q[4 * g + 1], v.y, sh);
+                sh = fmaf(q[4 * g + 2], v.z, sh);
+                sh = fmaf(q[4 * g + 3], v.w, sh);
+            }
+            const float sq = fmaf(sh, 0.0625f, sl);
             acc[b] = fmaf(scale, fmaf(-8.0f, xsum[b * NP + p], sq), acc[b]);
         }
     }
@@ -202,22 +229,22 @@ __device__ __forceinline__ float packet_dot_reg(const uint4 raw, float scale,
         for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], xv[e], acc);
         return acc;
     } else {
+        // low nibbles as bytes (q), high nibbles in place (16 q), see packet_dot
         const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-        float sq = 0.0f;
+        float sl = 0.0f, sh = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
+            const uint32_t lo = and_word(words[m], 0x0F0F0F0Fu);
 #pragma unroll
-            for (int n = 0; n < 4; ++n) sq = fmaf((float)((lo >> (8 * n)) & 0xFFu), xv[4 * m + n], sq);
+            for (int n = 0; n < 4; ++n) sl = fmaf(byte_to_float(lo, n), xv[4 * m + n], sl);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t hi = and_word(words[m], 0xF0F0F0F0u);
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-                sq = fmaf((float)((hi >> (8 * n)) & 0xFFu), xv[16 + 4 * m + n], sq);
+            for (int n = 0; n < 4; ++n) sh = fmaf(byte_to_float(hi, n), xv[16 + 4 * m + n], sh);
         }
-        return fmaf(scale, fmaf(-8.0f, xsum, sq), acc);
+        return fmaf(scale, fmaf(-8.0f, xsum, fmaf(sh, 0.0625f, sl)), acc);
     }
 }
 
@@ -237,17 +264,60 @@ __device__ __forceinline__ void packet_values(const uint4 raw, float scale,
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[e] = (float)h[e];
     } else {
+        // (q - 8) s, with the high nibbles read in place as 16 q: 16 q s / 16
+        // - 8 s is computed as (16 q - 128) (s / 16), exact up to the one rounding
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float s16 = scale * 0.0625f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = and_word(words[m], 0x0F0F0F0Fu);
+            const uint32_t hi = and_word(words[m], 0xF0F0F0F0u);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                w[4 * m + n] = (byte_to_float(lo, n) - 8.0f) * scale;
+                w[16 + 4 * m + n] = (byte_to_float(hi, n) - 128.0f) * s16;
+            }
+        }
+    }
+}
+
+// acc[e] += a * (weight e of the packet).  For 4-bit packets the "- 8" of every
+// code is left out and summed in `corr` instead (corr += a * scale), so each
+// weight costs one widening and one multiply-add; the caller finishes with
+// acc[e] -= 8 corr.  High nibbles are read in place (16 q) against a / 16,
+// which gives the same product as q against a.
+template <int FMT>
+__device__ __forceinline__ void packet_axpy(const uint4 raw, float scale, float a,
+                                            float (&acc)[PacketElems<FMT>::value], float &corr) {
+    if constexpr (FMT == kQ4) {
+        const float as = a * scale, as16 = as * 0.0625f;
         const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t lo = words[m] & 0x0F0F0F0Fu;
-            const uint32_t hi = (words[m] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lo = and_word(words[m], 0x0F0F0F0Fu);
+            const uint32_t hi = and_word(words[m], 0xF0F0F0F0u);
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
-                w[4 * m + n] = ((float)((lo >> (8 * n)) & 0xFFu) - 8.0f) * scale;
-                w[16 + 4 * m + n] = ((float)((hi >> (8 * n)) & 0xFFu) - 8.0f) * scale;
+                acc[4 * m + n] = fmaf(as, byte_to_float(lo, n), acc[4 * m + n]);
+                acc[16 + 4 * m + n] = fmaf(as16, byte_to_float(hi, n), acc[16 + 4 * m + n]);
             }
         }
+        corr += as;
+    } else {
+        float w[PacketElems<FMT>::value];
+        packet_values<FMT>(raw, scale, w);
+#pragma unroll
+        for (int e = 0; e < PacketElems<FMT>::value; ++e) acc[e] = fmaf(a, w[e], acc[e]);
+    }
+}
+
+// Finish packet_axpy's accumulation: apply the summed "- 8" of 4-bit codes.
+template <int FMT>
+__device__ __forceinline__ void packet_axpy_finish(float (&acc)[PacketElems<FMT>::value],
+                                                   float corr) {
+    if constexpr (FMT == kQ4) {
+#pragma unroll
+        for (int e = 0; e < PacketElems<FMT>::value; ++e) acc[e] = fmaf(-8.0f, corr, acc[e]);
     }
 }
 

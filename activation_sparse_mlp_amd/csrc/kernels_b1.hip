@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void down_b1_kernel(DownB1Args a) {
     const int per = (cnt + a.chunks - 1) / a.chunks;
     const int j0 = min(cnt, c * per), j1 = min(cnt, j0 + per);
 
-    float acc[E];
+    float acc[E], corr = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
@@ -330,15 +330,11 @@ __global__ __launch_bounds__(256) void down_b1_kernel(DownB1Args a) {
                 if (!ok) av[u] = 0.0f;
             }
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                float w[E];
-                packet_values<FMT>(raw[u], sc[u], w);
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = fmaf(av[u], w[e], acc[e]);
-            }
+            for (int u = 0; u < UR; ++u) packet_axpy<FMT>(raw[u], sc[u], av[u], acc, corr);
         }
     }
 
+    packet_axpy_finish<FMT>(acc, corr);
     // fixed-order reduction of the four waves through LDS
     for (int w = 0; w < 4; ++w) {
         if (wv == w) {
@@ -618,7 +614,7 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
         }
     }
 
-    float acc[E];
+    float acc[E], corr = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
@@ -653,15 +649,11 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
                 if (!ok) av[u] = 0.0f;
             }
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                float w[E];
-                packet_values<FMT>(raw[u], sc[u], w);
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = fmaf(av[u], w[e], acc[e]);
-            }
+            for (int u = 0; u < UR; ++u) packet_axpy<FMT>(raw[u], sc[u], av[u], acc, corr);
         }
     }
 
+    packet_axpy_finish<FMT>(acc, corr);
     for (int w = 0; w < 4; ++w) {
         if (wv == w) {
 #pragma unroll
@@ -791,10 +783,16 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
 // let the hardware hand new groups to CUs whose groups had few active rows,
 // which balances the gather phase better than larger groups.
 constexpr int kFusedRW = 2;
+// 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
+// row still reads the whole fp32 activation vector (and its block sums), so
+// their groups are larger (16 rows) to spread that read over more active rows
+// (measured at the 175B-shaped layer: 8 rows 57 us, 16 rows 52.5, 32 rows 55.7).
+constexpr int kFusedRWQ4 = 4;
+
+template <int FMT> constexpr int fused_rw() { return FMT == kQ4 ? kFusedRWQ4 : kFusedRW; }
 
 int fused_rows_per_group(const Layer &L) {
-    (void)L;
-    return 4 * kFusedRW;
+    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4 : kFusedRW);
 }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
@@ -837,9 +835,10 @@ static void launch_fused_t(const FusedArgs &a, int G, hipStream_t s, hipEvent_t 
 template <int PF, int FMT, bool GATED>
 static void launch_fused_rw(const FusedArgs &a, int G, int UA, hipStream_t s, hipEvent_t e0,
                             hipEvent_t e1) {
-    if (UA == 2) launch_fused_t<PF, FMT, GATED, kFusedRW, 2>(a, G, s, e0, e1);
-    else if (UA == 4) launch_fused_t<PF, FMT, GATED, kFusedRW, 4>(a, G, s, e0, e1);
-    else launch_fused_t<PF, FMT, GATED, kFusedRW, 8>(a, G, s, e0, e1);
+    constexpr int RW = fused_rw<FMT>();
+    if (UA == 2) launch_fused_t<PF, FMT, GATED, RW, 2>(a, G, s, e0, e1);
+    else if (UA == 4) launch_fused_t<PF, FMT, GATED, RW, 4>(a, G, s, e0, e1);
+    else launch_fused_t<PF, FMT, GATED, RW, 8>(a, G, s, e0, e1);
 }
 
 template <int PF, int FMT>
