@@ -229,7 +229,8 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     // fp16 splits of the batched path (only when it applies)
     const bool mf = B > 1 && mfma_fits(L, B);
     lo.ld_act = (D.d_ffn + 7) / 8 * 8;
-    const size_t nx = mf ? (size_t)B * D.d * 2 : 0, nh = mf ? (size_t)B * D.r * 2 : 0;
+    // packed B operands: 16 columns x K halves each (hi; lo for B > 8)
+    const size_t nx = mf ? (size_t)16 * D.d * 2 : 0, nh = mf ? (size_t)16 * D.r * 2 : 0;
     const size_t na = mf ? (size_t)B * lo.ld_act * 2 : 0;
     lo.xhi = off;
     off += up256(nx);

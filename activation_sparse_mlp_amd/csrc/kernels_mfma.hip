@@ -14,6 +14,11 @@
 //     B <= 8 the hi and lo parts of the B tokens share one instruction
 //     (columns 0..7 and 8..15) and the two halves of the result are added,
 //     for B > 8 they take one instruction each into the same accumulator;
+//   * the producers of those halves store them already in the instruction's
+//     B layout ("packed", bpack_index), so that one load instruction reads
+//     1 KB of contiguous memory; in token-major order each instruction would
+//     touch 16 separate 64-byte pieces, and every wave of every workgroup
+//     reads the same few lines at the same time;
 //   * accumulation is fp32 throughout.
 //
 // Operand layouts of the instruction (wave64), checked on the device:
@@ -47,8 +52,28 @@ __device__ __forceinline__ half8 ld_half8(const _Float16 *p) {
     return as_half8(*reinterpret_cast<const uint4 *>(p));
 }
 
+// Packed B operand of 16 columns and K rows (K a multiple of 128): per 128-row
+// step and per 32-row instruction s, lane l = 16q + m holds column m, rows
+// 32s + 8q .. +7, as 16 contiguous bytes; 2048 halves per step.  Column m is
+// token m's hi half (or, for B <= 8, token m - 8's lo half when m >= 8).
+constexpr int kPackStep = 2048;
+__device__ __forceinline__ size_t bpack_index(int m, int k) {
+    return ((size_t)((k >> 7) * 4 + ((k >> 5) & 3)) * 64 + ((k >> 3) & 3) * 16 + m) * 8 + (k & 7);
+}
+
+// Store value v of token b, row k: hi and lo halves, into p0 (and p1 for B > 8).
+__device__ __forceinline__ void bpack_store(_Float16 *p0, _Float16 *p1, int B, int b, int k,
+                                            float v) {
+    const _Float16 h = (_Float16)v;
+    const _Float16 l = (_Float16)(v - (float)h);
+    p0[bpack_index(b, k)] = h;
+    if (B > 8) p1[bpack_index(b, k)] = l;
+    else p0[bpack_index(b + 8, k)] = l;
+}
+
 // ---------------------------------------------------------------------------
-// x [B, K] fp32 -> (optionally RMS-normalised) n, and its hi/lo fp16 split.
+// x [B, K] fp32 -> (optionally RMS-normalised) n, and its hi/lo fp16 split
+// in the packed B-operand layout (hi: 16 x K halves; lo: used for B > 8).
 // Block (b, c) writes columns [c K/C, (c+1) K/C) of token b; with
 // normalisation every block of a token first sums the token's squares in the
 // same fixed order, so all of them use the same scale.
@@ -84,11 +109,8 @@ __global__ __launch_bounds__(256) void split_act_kernel(const float *__restrict_
     const int c0 = blockIdx.y * per;
     for (int k = c0 + threadIdx.x; k < c0 + per; k += blockDim.x) {
         const float v = xb[k] * s;
-        const _Float16 h = (_Float16)v;
-        const size_t o = (size_t)b * K + k;
-        if (n_out) n_out[o] = v;
-        hi[o] = h;
-        lo[o] = (_Float16)(v - (float)h);
+        if (n_out) n_out[(size_t)b * K + k] = v;
+        bpack_store(hi, lo, gridDim.x, b, k, v);
     }
 }
 
@@ -109,7 +131,7 @@ struct BgArgs {
     int rows;              // rows of the matrix
     const int32_t *idx;    // gathered: row of list entry j; nullptr: dense
     const int32_t *count;  // device count of the list (gathered only)
-    const _Float16 *xhi, *xlo;  // [B, K]
+    const _Float16 *xhi, *xlo;  // packed B operand (bpack_index), 16 x K halves each
     int B;
     // epilogues
     const float *bias;     // [rows] or nullptr (mask: b2; act: b_act)
@@ -156,13 +178,12 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             pa[t][g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
             pu[t][g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
         }
-    // B operand source of this lane: token m (SPLIT2), or token m & 7 of the
-    // hi (m < 8) / lo (m >= 8) half; columns 32s + 8q of each 128
+    // B operand of this lane (packed): token m (SPLIT2), or token m & 7 of the
+    // hi (m < 8) / lo (m >= 8) half, from the wave's first 128-row step on
     const int tok = SPLIT2 ? m : (m & 7);
     const bool tv = tok < a.B;
-    const _Float16 *px = (SPLIT2 || m < 8 ? a.xhi : a.xlo) + (size_t)(tv ? tok : 0) * a.K + k0 +
-                         8 * q;
-    const _Float16 *pxl = a.xlo + (size_t)(tv ? tok : 0) * a.K + k0 + 8 * q;
+    const _Float16 *px = a.xhi + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
+    const _Float16 *pxl = a.xlo + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
 
     f32x4 ca[T], cu[T];
 #pragma unroll
@@ -183,8 +204,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
         half8 xb[4], xl[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            xb[s] = tv ? ld_half8(px + kb + 32 * s) : zero8;
-            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + kb + 32 * s) : zero8;
+            const size_t o = (size_t)(kb >> 7) * kPackStep + 512 * s;
+            xb[s] = tv ? ld_half8(px + o) : zero8;
+            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + o) : zero8;
         }
 #pragma unroll
         for (int t = 0; t < T; ++t)
@@ -271,7 +293,8 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     }
 }
 
-// hid[b, i] = ReLU(sum over the K splits of part + b1[i]), fp32 and split.
+// hid[b, i] = ReLU(sum over the K splits of part + b1[i]), fp32 and split
+// (packed B operand of predictor layer 2).
 __global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict__ part, int KS,
                                                         int B, int r, const float *__restrict__ b1,
                                                         float *__restrict__ hid,
@@ -284,9 +307,7 @@ __global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict_
     for (int c = 0; c < KS; ++c) v += part[(size_t)c * B * r + t];
     v = fmaxf(v + (b1 ? b1[i] : 0.0f), 0.0f);
     hid[t] = v;
-    const _Float16 h = (_Float16)v;
-    hhi[t] = h;
-    hlo[t] = (_Float16)(v - (float)h);
+    bpack_store(hhi, hlo, B, t / r, i, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -294,12 +315,15 @@ __global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict_
 // act[b, j] * W_down_t[idx[j], col], for the block's 512 columns.  Chunk c is
 // entries [c*per, (c+1)*per) with per = the list length over the chunks,
 // rounded up to a multiple of 32 (from the device count, so every chunk has
-// work whatever the list length).  Per step the block stages
-// 32 gathered rows x 512 columns (fp16) in LDS; wave w then owns columns
-// w*128 .. w*128+127 (8 tiles of 16) and reads its B operands transposed.
+// work whatever the list length).  Per step the block stages 32 gathered rows
+// x 512 columns (fp16) in LDS, rows 2p and 2p + 1 interleaved column by column
+// (one 32-bit word holds both), so that a lane's B operand -- 8 consecutive
+// rows of one column -- is four 32-bit LDS reads; wave w owns columns
+// w*128 .. w*128+127 (8 tiles of 16).  The weights of the next two steps and
+// the row indices of the one after are in flight during the multiplies.
 // ---------------------------------------------------------------------------
 constexpr int kDownCols = 512;
-constexpr int kDownPitch = kDownCols + 8;  // halves per staged row (16-byte aligned)
+constexpr int kDownPitch = kDownCols + 4;  // words per staged row pair
 
 struct BdArgs {
     const _Float16 *wd;  // W_down_t [rows, d]
@@ -310,9 +334,22 @@ struct BdArgs {
     float *part;  // [gridDim.y, B, d]
 };
 
+// Interleave two rows' 8 halves: word e = (lo: a[e], hi: b[e]).
+__device__ __forceinline__ void interleave_rows(uint4 ra, uint4 rb, uint4 &w0, uint4 &w1) {
+    const uint32_t x[4] = {ra.x, ra.y, ra.z, ra.w}, y[4] = {rb.x, rb.y, rb.z, rb.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = (x[i] & 0xFFFFu) | (y[i] << 16);
+        o[2 * i + 1] = (x[i] >> 16) | (y[i] & 0xFFFF0000u);
+    }
+    w0 = make_uint4(o[0], o[1], o[2], o[3]);
+    w1 = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 template <bool SPLIT2>
 __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
-    __shared__ __align__(16) _Float16 tile[32 * kDownPitch];
+    __shared__ __align__(16) uint32_t tile[16 * kDownPitch];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, q = lane >> 4;
     const int slice = blockIdx.x, c = blockIdx.y;
@@ -330,14 +367,13 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
     const bool tv = tok < a.B;
     const _Float16 *pa = (SPLIT2 || m < 8 ? a.ahi : a.alo) + (size_t)(tv ? tok : 0) * a.ld_act;
     const _Float16 *pal = a.alo + (size_t)(tv ? tok : 0) * a.ld_act;
-    // Thread t stages packet p = t & 63 of step rows (t >> 6) + 4u, u < 8.
-    // Software pipeline: the next step's row indices and weights are in
-    // flight while the current step's tile is multiplied.
+    // Thread t stages packet p = t & 63 (8 columns) of the step's row pairs
+    // pr = (t >> 6) + 4u, u < 4: rows 2 pr and 2 pr + 1.
     const int p = threadIdx.x & 63, r0 = threadIdx.x >> 6;
     auto rows_of = [&](int kb, int (&rv)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int jj = kb + r0 + 4 * u;
+            const int jj = kb + 2 * (r0 + 4 * (u >> 1)) + (u & 1);
             int row = jj < j1 ? (a.idx ? a.idx[jj] : jj) : -1;
             rv[u] = row < 0 ? -1 : min(row, a.rows - 1);
         }
@@ -351,19 +387,31 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
             vv[u] = rv[u] >= 0 ? w : make_uint4(0, 0, 0, 0);
         }
     };
-    int rowv[8];
-    uint4 v[8];
-    rows_of(j0, rowv);
-    load_w(rowv, v);
-    for (int kb = j0; kb < j1; kb += 32) {
-        int nrow[8];
-        rows_of(kb + 32, nrow);
+    // Two weight buffers alternate (a: steps j0, j0 + 64, ...; b: j0 + 32, ...):
+    // while step kb is multiplied, the weights of kb + 32 (other buffer) and
+    // kb + 64 (this buffer, refilled right after it is staged) are in flight,
+    // and each buffer's row indices are read one of its steps ahead.
+    int ra[8], rb[8];
+    uint4 va[8], vb[8];
+    rows_of(j0, ra);
+    load_w(ra, va);
+    rows_of(j0 + 32, rb);
+    load_w(rb, vb);
+    rows_of(j0 + 64, ra);
+    rows_of(j0 + 96, rb);
+    auto step = [&](int kb, uint4 (&v)[8], int (&rv)[8]) {
         __syncthreads();  // the previous step's reads of the tile are done
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            *reinterpret_cast<uint4 *>(&tile[(r0 + 4 * u) * kDownPitch + 8 * p]) = v[u];
+        for (int u = 0; u < 4; ++u) {
+            uint4 w0, w1;
+            interleave_rows(v[2 * u], v[2 * u + 1], w0, w1);
+            uint32_t *dst = &tile[(r0 + 4 * u) * kDownPitch + 8 * p];
+            *reinterpret_cast<uint4 *>(dst) = w0;
+            *reinterpret_cast<uint4 *>(dst + 4) = w1;
+        }
         __syncthreads();
-        load_w(nrow, v);
+        load_w(rv, v);           // step kb + 64
+        rows_of(kb + 128, rv);   // the buffer's step after that
         // A: act of list entries kb + 8q .. +7 (zero past j1)
         half8 av, avl;
         const int ja = kb + 8 * q;
@@ -381,12 +429,20 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cc = wv * 128 + t * 16 + m;  // column within the slice
-            half8 bv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bv[i] = tile[(8 * q + i) * kDownPitch + cc];
+            // rows 8q .. 8q+7 of column cc: row pairs 4q .. 4q+3
+            uint4 bw;
+            bw.x = tile[(4 * q + 0) * kDownPitch + cc];
+            bw.y = tile[(4 * q + 1) * kDownPitch + cc];
+            bw.z = tile[(4 * q + 2) * kDownPitch + cc];
+            bw.w = tile[(4 * q + 3) * kDownPitch + cc];
+            const half8 bv = as_half8(bw);
             acc[t] = mfma16x16x32(av, bv, acc[t]);
             if constexpr (SPLIT2) acc[t] = mfma16x16x32(avl, bv, acc[t]);
         }
+    };
+    for (int kb = j0; kb < j1; kb += 64) {
+        step(kb, va, ra);
+        if (kb + 32 < j1) step(kb + 32, vb, rb);
     }
 
     // D lane (m, q): tokens 4q + i, column m of the tile.  B <= 8: rows 8..15
@@ -411,13 +467,19 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
 constexpr int kBgWaves = 4;
 constexpr int kW1Splits = 8;  // K splits of predictor layer 1 (few rows, long K)
 constexpr int kBdChunks = 32;
+// The gathered gate/up products have few row tiles (one per 16 listed rows)
+// and a long K, so each tile gets more waves: as many as the 64 KB of staging
+// LDS allows (16 for one matrix, 8 for gate and up; half that at B > 8).
+constexpr int kGatherWaves = 16, kGatherWavesG = 8;
 
 bool mfma_fits(const Layer &L, int B) {
     const spffn_layer_desc &D = L.desc;
     if (B < 2 || B > 16) return false;
     if (D.w_dtype != SPFFN_F16 || D.p_dtype != SPFFN_F16) return false;
-    const int kstep = 128 * kBgWaves;  // each wave's K range is whole 128-column steps
-    return D.d % (kstep * kW1Splits) == 0 && D.r % kstep == 0 && D.d % kDownCols == 0;
+    // every wave's K range is whole 128-column steps
+    const int kstep = 128 * kBgWaves;
+    return D.d % (kstep * kW1Splits) == 0 && D.r % kstep == 0 && D.d % kDownCols == 0 &&
+           D.d % (128 * kGatherWaves) == 0;
 }
 
 int mfma_down_chunks() { return kBdChunks; }
@@ -434,13 +496,14 @@ hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normal
 // Two 16-row tiles per workgroup when B > 8 (the activation operand then
 // costs as many bytes as the weights, so sharing it halves that traffic);
 // grid.x counts 16-row tiles and is rounded to the workgroup's tiles here.
-template <bool GATED, int EPI>
+// WV1 / WV2: waves per workgroup for B <= 8 / B > 8 (each wave a K range).
+template <bool GATED, int EPI, int WV1, int WV2>
 static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
     if (a.B > 8) {
         grid.x = (grid.x + 1) / 2;
-        bgemv_kernel<kBgWaves, 2, GATED, true, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+        bgemv_kernel<WV2, 2, GATED, true, EPI><<<grid, 64 * WV2, 0, s>>>(a);
     } else {
-        bgemv_kernel<kBgWaves, 1, GATED, false, EPI><<<grid, 64 * kBgWaves, 0, s>>>(a);
+        bgemv_kernel<WV1, 1, GATED, false, EPI><<<grid, 64 * WV1, 0, s>>>(a);
     }
 }
 
@@ -456,7 +519,7 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     a.xlo = xlo;
     a.B = B;
     a.part = w1part;
-    launch_bg<false, kEpiPartial>(a, dim3((D.r + 15) / 16, kW1Splits), s);
+    launch_bg<false, kEpiPartial, kBgWaves, kBgWaves>(a, dim3((D.r + 15) / 16, kW1Splits), s);
     w1_finish_kernel<<<(B * D.r + 255) / 256, 256, 0, s>>>(w1part, kW1Splits, B, D.r, D.p_b1, hid,
                                                           hhi, hlo);
     BgArgs b{};
@@ -471,7 +534,7 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     b.logits = logits;
     b.mask = mask;
     b.uni = uni;
-    launch_bg<false, kEpiMask>(b, dim3((D.d_ffn + 15) / 16, 1), s);
+    launch_bg<false, kEpiMask, kBgWaves, kBgWaves>(b, dim3((D.d_ffn + 15) / 16, 1), s);
     return hipGetLastError();
 }
 
@@ -495,8 +558,8 @@ hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *
     a.alo = alo;
     a.ld_act = ld_act;
     const dim3 grid((D.d_ffn + 15) / 16, 1);
-    if (gated) launch_bg<true, kEpiAct>(a, grid, s);
-    else launch_bg<false, kEpiAct>(a, grid, s);
+    if (gated) launch_bg<true, kEpiAct, kGatherWavesG, kGatherWavesG / 2>(a, grid, s);
+    else launch_bg<false, kEpiAct, kGatherWaves, kGatherWaves / 2>(a, grid, s);
 
     BdArgs b{};
     b.wd = reinterpret_cast<const _Float16 *>(L.down.data);
