@@ -69,6 +69,7 @@ struct Ws {
     uint8_t *mask, *uni;
     int32_t *idx, *count, *gcnt, *lst_i;
     _Float16 *xhi, *xlo, *hhi, *hlo, *ahi, *alo;
+    uint16_t *tmask;
     int ld_act;
     int chunks;
 };
@@ -96,6 +97,7 @@ Ws carve(const Layer &L, int B, void *ws) {
     w.hlo = reinterpret_cast<_Float16 *>(base + lo.hlo);
     w.ahi = reinterpret_cast<_Float16 *>(base + lo.ahi);
     w.alo = reinterpret_cast<_Float16 *>(base + lo.alo);
+    w.tmask = reinterpret_cast<uint16_t *>(base + lo.tmask);
     w.ld_act = lo.ld_act;
     w.chunks = lo.chunks;
     return w;
@@ -121,9 +123,12 @@ bool single(const Layer &L, int B) { return B == 1 && b1_fits(L); }
 // x is normalised by `scale` (device, per token) when scale != nullptr; the
 // output is written to y, plus resid when resid != nullptr.
 // split_ready: the batched path's fp16 split of x is already in w.xhi/xlo.
+// tiles: (matrix-core path) the rows are the union rows marked in w.tmask
+// instead of (idx, count); their list goes to w.idx / w.count (and count2).
 spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
                      const int32_t *idx, const int32_t *count, const float *resid, float *y,
-                     const Ws &w, hipStream_t s, bool split_ready = false) {
+                     const Ws &w, hipStream_t s, bool split_ready = false, bool tiles = false,
+                     int32_t *count2 = nullptr) {
     if (single(L, B)) {
         SPFFN_HIP(launch_up_b1(L, x, scale, idx, count, w.act, s), "gather up/gate launch");
         SPFFN_HIP(launch_down_b1(L, idx, count, w.act, w.part, w.chunks, s), "gather down launch");
@@ -135,9 +140,14 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
         if (!split_ready)
             SPFFN_HIP(launch_split_act(x, B, L.desc.d, 0.0f, false, nullptr, w.xhi, w.xlo, s),
                       "split launch");
-        SPFFN_HIP(launch_mfma_ffn(L, w.xhi, w.xlo, B, idx, count, w.ahi, w.alo, w.ld_act, w.part,
-                                  s),
-                  "batched gather launch");
+        if (tiles)
+            SPFFN_HIP(launch_mfma_ffn_tiles(L, w.xhi, w.xlo, B, w.tmask, w.idx, w.count, count2,
+                                            w.ahi, w.alo, w.ld_act, w.part, s),
+                      "batched gather launch");
+        else
+            SPFFN_HIP(launch_mfma_ffn(L, w.xhi, w.xlo, B, idx, count, w.ahi, w.alo, w.ld_act,
+                                      w.part, s),
+                      "batched gather launch");
         SPFFN_HIP(launch_reduce_groups(w.part, mfma_down_chunks(), (int64_t)B * L.desc.d, resid,
                                        y, s),
                   "reduce launch");
@@ -152,10 +162,11 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
 }
 
 // Predictor of B tokens.  normalize: x is the residual stream and is RMS
-// normalised first (decode); the RMS scale goes to w.scale.
+// normalised first (decode); the RMS scale goes to w.scale.  tiles: the
+// matrix-core path also writes the union bits per 16-row tile to w.tmask.
 spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, float eps,
                          float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s,
-                         bool split_ready = false) {
+                         bool split_ready = false, bool tiles = false) {
     const spffn_layer_desc &D = L.desc;
     if (single(L, B)) {
         SPFFN_HIP(launch_w1_b1(L, x, eps, normalize, w.hid, w.scale, s), "predictor layer-1 launch");
@@ -170,7 +181,7 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
             SPFFN_HIP(launch_split_act(x, B, D.d, eps, normalize, w.n, w.xhi, w.xlo, s),
                       "split launch");
         SPFFN_HIP(launch_mfma_predict(L, w.xhi, w.xlo, B, w.w1p, w.hid, w.hhi, w.hlo, logits, mask,
-                                      uni, s),
+                                      uni, tiles ? w.tmask : nullptr, s),
                   "batched predictor launch");
         return SPFFN_OK;
     }
@@ -246,6 +257,8 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     off += up256(na);
     lo.w1p = off;
     off += up256(mf ? (size_t)mfma_w1_splits() * B * D.r * 4 : 0);
+    lo.tmask = off;
+    off += up256(mf ? (size_t)(D.d_ffn + 15) / 16 * 2 : 0);
     lo.total = off;
     return lo;
 }
@@ -586,11 +599,14 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         else if (!one)
             SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
         if (!dense) {
-            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf)))
+            // the matrix-core gather lists the union rows itself (from tile
+            // masks of the predictor's last kernel); other paths compact
+            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf, mf)))
                 return st;
-            SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,
-                                     layer_counts ? layer_counts + l : nullptr),
-                      "compact launch");
+            if (!mf)
+                SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,
+                                         layer_counts ? layer_counts + l : nullptr),
+                          "compact launch");
             if (trace && trace->union_mask)
                 SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F,
                                          hipMemcpyDeviceToDevice, s),
@@ -604,7 +620,9 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         }
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
-        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s, mf))) return st;
+        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s, mf, mf && !dense,
+                          layer_counts ? layer_counts + l : nullptr)))
+            return st;
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
         mask_off += F;

@@ -34,6 +34,7 @@ struct Layer {
 struct WsLayout {
     size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, part, total;
     size_t xhi, xlo, hhi, hlo, ahi, alo, w1p;  // fp16 splits and partials of the batched path
+    size_t tmask;                              // union bits per 16-row tile (batched path)
     int ld_act;  // row pitch (elements) of ahi / alo
     int chunks;  // neuron chunks of the down projection (partial-sum slots)
 };
@@ -94,12 +95,20 @@ int mfma_down_chunks();
 int mfma_w1_splits();
 hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
                             _Float16 *hi, _Float16 *lo, hipStream_t s);
+// tmask (or nullptr): the union bits of each 16-row tile, for launch_mfma_ffn_tiles
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
-                               float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s);
+                               float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
+                               hipStream_t s);
 hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                            const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
                            int ld_act, float *part, hipStream_t s);
+// The same over the union rows given by tile masks; the list is built on the
+// device and written to idx[0..*count) (and *count2 when given).
+hipError_t launch_mfma_ffn_tiles(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                                 const uint16_t *tmask, int32_t *idx, int32_t *count,
+                                 int32_t *count2, _Float16 *ahi, _Float16 *alo, int ld_act,
+                                 float *part, hipStream_t s);
 
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s);

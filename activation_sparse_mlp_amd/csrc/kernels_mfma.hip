@@ -131,6 +131,13 @@ struct BgArgs {
     int rows;              // rows of the matrix
     const int32_t *idx;    // gathered: row of list entry j; nullptr: dense
     const int32_t *count;  // device count of the list (gathered only)
+    // Gathered from tile masks instead (tmask != nullptr): bit r of tmask[t]
+    // marks row 16t + r; list entry j is the j-th marked row in ascending
+    // order.  The kernel then writes the list it used to idx_out and its
+    // length to *count_out (and *count_out2 when given).
+    const uint16_t *tmask;
+    int ntiles;
+    int32_t *idx_out, *count_out, *count_out2;
     const _Float16 *xhi, *xlo;  // packed B operand (bpack_index), 16 x K halves each
     int B;
     // epilogues
@@ -140,6 +147,7 @@ struct BgArgs {
     float *logits;         // mask: [B, rows] or nullptr
     uint8_t *mask;         // mask: [B, rows] or nullptr
     uint8_t *uni;          // mask: [rows] or nullptr
+    uint16_t *tmask_out;   // mask: union bits of each 16-row tile, or nullptr
     _Float16 *ahi, *alo;   // act: [B, ld_act], entry j of the list
     int ld_act;
 };
@@ -154,142 +162,217 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     // cross-wave sums once the K loop is done.
     __shared__ uint4 stg[WV][NM][T][16][16];
     __shared__ uint32_t s_any[16 * T];
+    __shared__ int s_rows[16 * T];
+    __shared__ int s_wsum[WV];
     float(*red)[NM][T][256] = reinterpret_cast<float(*)[NM][T][256]>(&stg[0][0][0][0][0]);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, q = lane >> 4;
-    const int n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
-    const int j0 = blockIdx.x * 16 * T;
-    if (j0 >= n_items) return;  // whole block: the grid covers the largest list
-
     const int Kw = a.K / (WV * gridDim.y);
     const int k0 = (blockIdx.y * WV + wv) * Kw;
-    // Weight loads are row-contiguous: load g (of 4) gives lane l chunk l & 15
-    // (8 columns) of tile row 4g + (l >> 4), i.e. 256 contiguous bytes of each
-    // of 4 rows per instruction.  Through LDS each lane then picks up the
-    // chunks of the A layout (row m, columns 32s + 8q).
-    const _Float16 *pa[T][4], *pu[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int jr = j0 + 16 * t + 4 * g + (lane >> 4);
-            int rr = jr < n_items ? (a.idx ? a.idx[jr] : jr) : (a.idx ? a.idx[j0] : j0);
-            rr = min(max(rr, 0), a.rows - 1);
-            pa[t][g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
-            pu[t][g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
-        }
-    // B operand of this lane (packed): token m (SPLIT2), or token m & 7 of the
-    // hi (m < 8) / lo (m >= 8) half, from the wave's first 128-row step on
-    const int tok = SPLIT2 ? m : (m & 7);
-    const bool tv = tok < a.B;
-    const _Float16 *px = a.xhi + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
-    const _Float16 *pxl = a.xlo + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
 
-    f32x4 ca[T], cu[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) ca[t] = cu[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int kb = 0; kb < Kw; kb += 128) {
-        uint4 ga[T][4], gu[T][4];
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                ga[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                               reinterpret_cast<const u32x4_t *>(pa[t][g] + kb)));
-                if constexpr (GATED)
-                    gu[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                   reinterpret_cast<const u32x4_t *>(pu[t][g] + kb)));
-            }
-        half8 xb[4], xl[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const size_t o = (size_t)(kb >> 7) * kPackStep + 512 * s;
-            xb[s] = tv ? ld_half8(px + o) : zero8;
-            if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + o) : zero8;
+    // Length of the list.  From tile masks (gate/up products only): thread i
+    // owns tiles [i M, i M + M), whose marked rows take the ranks
+    // [base, base + own) of the list.
+    const bool from_tiles = EPI == kEpiAct && a.tmask;
+    int n_items, M = 0, own = 0, base = 0;
+    if (from_tiles) {
+        M = (a.ntiles + 64 * WV - 1) / (64 * WV);
+        for (int u = 0; u < M; ++u) {
+            const int t = (int)threadIdx.x * M + u;
+            if (t < a.ntiles) own += __popc((uint32_t)a.tmask[t]);
         }
+        int incl = own;
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
-                stg[wv][0][t][r][c] = ga[t][g];
-                if constexpr (GATED) stg[wv][NM - 1][t][r][c] = gu[t][g];
-            }
-        // the wave's own LDS writes are complete before any lane reads them
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = (4 * s + q) ^ m;
-                const half8 wa_ = as_half8(stg[wv][0][t][m][c]);
-                ca[t] = mfma16x16x32(wa_, xb[s], ca[t]);
-                if constexpr (SPLIT2) ca[t] = mfma16x16x32(wa_, xl[s], ca[t]);
-                if constexpr (GATED) {
-                    const half8 wu_ = as_half8(stg[wv][NM - 1][t][m][c]);
-                    cu[t] = mfma16x16x32(wu_, xb[s], cu[t]);
-                    if constexpr (SPLIT2) cu[t] = mfma16x16x32(wu_, xl[s], cu[t]);
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) s_wsum[wv] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int w = 0; w < WV; ++w) {
+            const int v = s_wsum[w];
+            before += w < wv ? v : 0;
+            total += v;
+        }
+        base = before + incl - own;
+        n_items = total;
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+            *a.count_out = total;
+            if (a.count_out2) *a.count_out2 = total;
+        }
+    } else {
+        n_items = a.idx ? min(max(*a.count, 0), a.rows) : a.rows;
+    }
+
+    // The grid may be smaller than the list (it is sized before the list is
+    // known): workgroups loop over row tiles.
+    for (int j0 = blockIdx.x * 16 * T; j0 < n_items; j0 += gridDim.x * 16 * T) {
+        if (from_tiles) {
+            // rows of list entries [j0, j0 + 16T), by the threads whose ranks cover them
+            const int lim = j0 + 16 * T;
+            if (own > 0 && base < lim && base + own > j0) {
+                int rank = base;
+                for (int u = 0; u < M && rank < lim; ++u) {
+                    const int t = (int)threadIdx.x * M + u;
+                    if (t >= a.ntiles) break;
+                    uint32_t mk = a.tmask[t];
+                    const int pop = __popc(mk);
+                    if (rank + pop <= j0) {
+                        rank += pop;
+                        continue;
+                    }
+                    while (mk) {
+                        const int b = __ffs(mk) - 1;
+                        mk &= mk - 1;
+                        if (rank >= j0 && rank < lim) s_rows[rank - j0] = 16 * t + b;
+                        ++rank;
+                    }
                 }
             }
-        // and all reads are done before the next step overwrites the slots
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    __syncthreads();  // every wave is done with its slots before they hold sums
-
-    // fixed-order sum over the waves: red[w][.][t][r*16 + n]
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            red[wv][0][t][(4 * q + i) * 16 + m] = ca[t][i];
-            if constexpr (GATED) red[wv][NM - 1][t][(4 * q + i) * 16 + m] = cu[t][i];
+            __syncthreads();
         }
-    if (threadIdx.x < 16 * T) s_any[threadIdx.x] = 0u;
-    __syncthreads();
-    // entry e < 256 T is (tile t = e / 256, row r = e / 16 % 16, column n =
-    // e % 16); for B <= 8 the entries n < 8 add the lo half held in column n + 8
-    for (int e = threadIdx.x; e < 256 * T; e += blockDim.x) {
-        const int t = e >> 8, te = e & 255, r = te >> 4, n = te & 15;
-        if (n >= a.B || (!SPLIT2 && n >= 8)) continue;
-        float za = 0.0f, zu = 0.0f;
-        for (int w = 0; w < WV; ++w) {
-            za += red[w][0][t][te];
-            if (!SPLIT2) za += red[w][0][t][te + 8];
-            if constexpr (GATED) {
-                zu += red[w][NM - 1][t][te];
-                if (!SPLIT2) zu += red[w][NM - 1][t][te + 8];
+        auto row_of = [&](int j) { return from_tiles ? s_rows[j - j0] : (a.idx ? a.idx[j] : j); };
+        // Weight loads are row-contiguous: load g (of 4) gives lane l chunk l & 15
+        // (8 columns) of tile row 4g + (l >> 4), i.e. 256 contiguous bytes of each
+        // of 4 rows per instruction.  Through LDS each lane then picks up the
+        // chunks of the A layout (row m, columns 32s + 8q).
+        const _Float16 *pa[T][4], *pu[T][4];
+    #pragma unroll
+        for (int t = 0; t < T; ++t)
+    #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int jr = j0 + 16 * t + 4 * g + (lane >> 4);
+                int rr = row_of(jr < n_items ? jr : j0);
+                rr = min(max(rr, 0), a.rows - 1);
+                pa[t][g] = a.wa + (size_t)rr * a.K + k0 + 8 * (lane & 15);
+                pu[t][g] = GATED ? a.wu + (size_t)rr * a.K + k0 + 8 * (lane & 15) : nullptr;
+            }
+        // B operand of this lane (packed): token m (SPLIT2), or token m & 7 of the
+        // hi (m < 8) / lo (m >= 8) half, from the wave's first 128-row step on
+        const int tok = SPLIT2 ? m : (m & 7);
+        const bool tv = tok < a.B;
+        const _Float16 *px = a.xhi + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
+        const _Float16 *pxl = a.xlo + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
+
+        f32x4 ca[T], cu[T];
+    #pragma unroll
+        for (int t = 0; t < T; ++t) ca[t] = cu[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int kb = 0; kb < Kw; kb += 128) {
+            uint4 ga[T][4], gu[T][4];
+    #pragma unroll
+            for (int t = 0; t < T; ++t)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    ga[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                   reinterpret_cast<const u32x4_t *>(pa[t][g] + kb)));
+                    if constexpr (GATED)
+                        gu[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                       reinterpret_cast<const u32x4_t *>(pu[t][g] + kb)));
+                }
+            half8 xb[4], xl[4];
+    #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const size_t o = (size_t)(kb >> 7) * kPackStep + 512 * s;
+                xb[s] = tv ? ld_half8(px + o) : zero8;
+                if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + o) : zero8;
+            }
+    #pragma unroll
+            for (int t = 0; t < T; ++t)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
+                    stg[wv][0][t][r][c] = ga[t][g];
+                    if constexpr (GATED) stg[wv][NM - 1][t][r][c] = gu[t][g];
+                }
+            // the wave's own LDS writes are complete before any lane reads them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    #pragma unroll
+            for (int t = 0; t < T; ++t)
+    #pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int c = (4 * s + q) ^ m;
+                    const half8 wa_ = as_half8(stg[wv][0][t][m][c]);
+                    ca[t] = mfma16x16x32(wa_, xb[s], ca[t]);
+                    if constexpr (SPLIT2) ca[t] = mfma16x16x32(wa_, xl[s], ca[t]);
+                    if constexpr (GATED) {
+                        const half8 wu_ = as_half8(stg[wv][NM - 1][t][m][c]);
+                        cu[t] = mfma16x16x32(wu_, xb[s], cu[t]);
+                        if constexpr (SPLIT2) cu[t] = mfma16x16x32(wu_, xl[s], cu[t]);
+                    }
+                }
+            // and all reads are done before the next step overwrites the slots
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        __syncthreads();  // every wave is done with its slots before they hold sums
+
+        // fixed-order sum over the waves: red[w][.][t][r*16 + n]
+    #pragma unroll
+        for (int t = 0; t < T; ++t)
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                red[wv][0][t][(4 * q + i) * 16 + m] = ca[t][i];
+                if constexpr (GATED) red[wv][NM - 1][t][(4 * q + i) * 16 + m] = cu[t][i];
+            }
+        if (threadIdx.x < 16 * T) s_any[threadIdx.x] = 0u;
+        __syncthreads();
+        // entry e < 256 T is (tile t = e / 256, row r = e / 16 % 16, column n =
+        // e % 16); for B <= 8 the entries n < 8 add the lo half held in column n + 8
+        for (int e = threadIdx.x; e < 256 * T; e += blockDim.x) {
+            const int t = e >> 8, te = e & 255, r = te >> 4, n = te & 15;
+            if (n >= a.B || (!SPLIT2 && n >= 8)) continue;
+            float za = 0.0f, zu = 0.0f;
+            for (int w = 0; w < WV; ++w) {
+                za += red[w][0][t][te];
+                if (!SPLIT2) za += red[w][0][t][te + 8];
+                if constexpr (GATED) {
+                    zu += red[w][NM - 1][t][te];
+                    if (!SPLIT2) zu += red[w][NM - 1][t][te + 8];
+                }
+            }
+            const int jj = j0 + 16 * t + r;
+            if (jj >= n_items) continue;
+            const int rr = row_of(jj);
+            if (from_tiles && n == 0) a.idx_out[jj] = rr;
+            if constexpr (EPI == kEpiPartial) {
+                a.part[((size_t)blockIdx.y * a.B + n) * a.rows + rr] = za;
+            } else if constexpr (EPI == kEpiMask) {
+                const float l = za + (a.bias ? a.bias[rr] : 0.0f);
+                const bool mk = l > a.t;
+                if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
+                if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
+                if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
+            } else {
+                float v = fmaxf(za + (a.bias ? a.bias[rr] : 0.0f), 0.0f);
+                if constexpr (GATED) v *= zu;
+                const _Float16 h = (_Float16)v;
+                a.ahi[(size_t)n * a.ld_act + jj] = h;
+                a.alo[(size_t)n * a.ld_act + jj] = (_Float16)(v - (float)h);
             }
         }
-        const int jj = j0 + 16 * t + r;
-        if (jj >= n_items) continue;
-        const int rr = a.idx ? a.idx[jj] : jj;
-        if constexpr (EPI == kEpiPartial) {
-            a.part[((size_t)blockIdx.y * a.B + n) * a.rows + rr] = za;
-        } else if constexpr (EPI == kEpiMask) {
-            const float l = za + (a.bias ? a.bias[rr] : 0.0f);
-            const bool mk = l > a.t;
-            if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
-            if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
-            if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
-        } else {
-            float v = fmaxf(za + (a.bias ? a.bias[rr] : 0.0f), 0.0f);
-            if constexpr (GATED) v *= zu;
-            const _Float16 h = (_Float16)v;
-            a.ahi[(size_t)n * a.ld_act + jj] = h;
-            a.alo[(size_t)n * a.ld_act + jj] = (_Float16)(v - (float)h);
+        if constexpr (EPI == kEpiMask) {
+            __syncthreads();
+            if ((int)threadIdx.x < 16 * T && a.uni && j0 + (int)threadIdx.x < n_items) {
+                const int jj = j0 + threadIdx.x;
+                a.uni[row_of(jj)] = (uint8_t)(s_any[threadIdx.x] != 0u);
+            }
+            // dense rows only: tile t of the workgroup is rows 16 (j0/16 + t) + r
+            if ((int)threadIdx.x < T && a.tmask_out && !a.idx &&
+                j0 + 16 * (int)threadIdx.x < n_items) {
+                uint32_t mk = 0;
+                for (int r = 0; r < 16; ++r) {
+                    const int jj = j0 + 16 * threadIdx.x + r;
+                    if (jj < n_items && s_any[16 * threadIdx.x + r] != 0u) mk |= 1u << r;
+                }
+                a.tmask_out[(j0 >> 4) + threadIdx.x] = (uint16_t)mk;
+            }
         }
-    }
-    if constexpr (EPI == kEpiMask) {
-        __syncthreads();
-        if ((int)threadIdx.x < 16 * T && a.uni && j0 + (int)threadIdx.x < n_items) {
-            const int jj = j0 + threadIdx.x;
-            a.uni[a.idx ? a.idx[jj] : jj] = (uint8_t)(s_any[threadIdx.x] != 0u);
-        }
+        __syncthreads();  // LDS is reused by the next row tile
     }
 }
 
@@ -471,6 +554,8 @@ constexpr int kBdChunks = 32;
 // and a long K, so each tile gets more waves: as many as the 64 KB of staging
 // LDS allows (16 for one matrix, 8 for gate and up; half that at B > 8).
 constexpr int kGatherWaves = 16, kGatherWavesG = 8;
+// workgroups of a gather whose list comes from tile masks (two per CU)
+constexpr int kGatherMaxTiles = 512;
 
 bool mfma_fits(const Layer &L, int B) {
     const spffn_layer_desc &D = L.desc;
@@ -509,7 +594,8 @@ static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
-                               float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s) {
+                               float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
+                               hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     BgArgs a{};
     a.wa = reinterpret_cast<const _Float16 *>(L.w1.data);
@@ -534,30 +620,22 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     b.logits = logits;
     b.mask = mask;
     b.uni = uni;
+    b.tmask_out = tmask;
     launch_bg<false, kEpiMask, kBgWaves, kBgWaves>(b, dim3((D.d_ffn + 15) / 16, 1), s);
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
-                           const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
-                           int ld_act, float *part, hipStream_t s) {
+// gate/up products over the list, then the down projection into part
+static hipError_t mfma_ffn(const Layer &L, BgArgs a, dim3 grid, const int32_t *idx,
+                           const int32_t *count, int B, float *part, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     const bool gated = D.kind == SPFFN_REGLU;
-    BgArgs a{};
     a.wa = reinterpret_cast<const _Float16 *>((gated ? L.gate : L.up).data);
     a.wu = reinterpret_cast<const _Float16 *>(L.up.data);
     a.K = D.d;
     a.rows = D.d_ffn;
-    a.idx = idx;
-    a.count = count;
-    a.xhi = xhi;
-    a.xlo = xlo;
     a.B = B;
     a.bias = D.b_act;
-    a.ahi = ahi;
-    a.alo = alo;
-    a.ld_act = ld_act;
-    const dim3 grid((D.d_ffn + 15) / 16, 1);
     if (gated) launch_bg<true, kEpiAct, kGatherWavesG, kGatherWavesG / 2>(a, grid, s);
     else launch_bg<false, kEpiAct, kGatherWaves, kGatherWaves / 2>(a, grid, s);
 
@@ -567,15 +645,49 @@ hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *
     b.rows = D.d_ffn;
     b.idx = idx;
     b.count = count;
-    b.ahi = ahi;
-    b.alo = alo;
-    b.ld_act = ld_act;
+    b.ahi = a.ahi;
+    b.alo = a.alo;
+    b.ld_act = a.ld_act;
     b.B = B;
     b.part = part;
     const dim3 gd(D.d / kDownCols, kBdChunks);
     if (B > 8) bdown_kernel<true><<<gd, 256, 0, s>>>(b);
     else bdown_kernel<false><<<gd, 256, 0, s>>>(b);
     return hipGetLastError();
+}
+
+hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                           const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
+                           int ld_act, float *part, hipStream_t s) {
+    BgArgs a{};
+    a.idx = idx;
+    a.count = count;
+    a.xhi = xhi;
+    a.xlo = xlo;
+    a.ahi = ahi;
+    a.alo = alo;
+    a.ld_act = ld_act;
+    return mfma_ffn(L, a, dim3((L.desc.d_ffn + 15) / 16, 1), idx, count, B, part, s);
+}
+
+hipError_t launch_mfma_ffn_tiles(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
+                                 const uint16_t *tmask, int32_t *idx, int32_t *count,
+                                 int32_t *count2, _Float16 *ahi, _Float16 *alo, int ld_act,
+                                 float *part, hipStream_t s) {
+    BgArgs a{};
+    a.tmask = tmask;
+    a.ntiles = (L.desc.d_ffn + 15) / 16;
+    a.idx_out = idx;
+    a.count_out = count;
+    a.count_out2 = count2;
+    a.xhi = xhi;
+    a.xlo = xlo;
+    a.ahi = ahi;
+    a.alo = alo;
+    a.ld_act = ld_act;
+    // at most one pass of resident workgroups; they loop over longer lists
+    const int tiles = min(a.ntiles, kGatherMaxTiles * (B > 8 ? 2 : 1));
+    return mfma_ffn(L, a, dim3(tiles, 1), idx, count, B, part, s);
 }
 
 }  // namespace spffn
