@@ -785,9 +785,10 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
 constexpr int kFusedRW = 2;
 // 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
 // row still reads the whole fp32 activation vector (and its block sums), so
-// their groups are larger (16 rows) to spread that read over more active rows
-// (measured at the 175B-shaped layer: 8 rows 57 us, 16 rows 52.5, 32 rows 55.7).
-constexpr int kFusedRWQ4 = 4;
+// their groups are larger (20 rows) to spread that read over more active rows
+// (measured at the 175B-shaped layer: 8 rows 55.5 us, 12 rows 51.4, 16 rows
+// 50.4-51.2, 20 rows 48.0-48.7, 24 rows 55.2, 28 rows 49.7, 32 rows 52.4).
+constexpr int kFusedRWQ4 = 5;
 
 template <int FMT> constexpr int fused_rw() { return FMT == kQ4 ? kFusedRWQ4 : kFusedRW; }
 
