@@ -27,6 +27,7 @@ def _model(cfg, layers):
     (TINY, 2, 1, False),          # fp32 rows, single-token fused path
     (LLAMA2_7B, 2, 1, False),     # fp16 rows, single-token fused path
     (LLAMA2_7B, 2, 4, False),     # batched union path
+    (LLAMA2_7B, 1, 12, False),    # batched, two row tiles per workgroup
     (LLAMA2_7B, 1, 1, True),      # dense baseline
 ])
 def test_graph_replays_match_eager(cfg, layers, B, dense):
