@@ -238,9 +238,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
         // of 4 rows per instruction.  Through LDS each lane then picks up the
         // chunks of the A layout (row m, columns 32s + 8q).
         const _Float16 *pa[T][4], *pu[T][4];
-    #pragma unroll
+#pragma unroll
         for (int t = 0; t < T; ++t)
-    #pragma unroll
+#pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int jr = j0 + 16 * t + 4 * g + (lane >> 4);
                 int rr = row_of(jr < n_items ? jr : j0);
@@ -256,14 +256,14 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
         const _Float16 *pxl = a.xlo + (size_t)(k0 >> 7) * kPackStep + 8 * lane;
 
         f32x4 ca[T], cu[T];
-    #pragma unroll
+#pragma unroll
         for (int t = 0; t < T; ++t) ca[t] = cu[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int kb = 0; kb < Kw; kb += 128) {
             uint4 ga[T][4], gu[T][4];
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < T; ++t)
-    #pragma unroll
+#pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     ga[t][g] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
                                    reinterpret_cast<const u32x4_t *>(pa[t][g] + kb)));
@@ -272,15 +272,15 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                                        reinterpret_cast<const u32x4_t *>(pu[t][g] + kb)));
                 }
             half8 xb[4], xl[4];
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const size_t o = (size_t)(kb >> 7) * kPackStep + 512 * s;
                 xb[s] = tv ? ld_half8(px + o) : zero8;
                 if constexpr (SPLIT2) xl[s] = tv ? ld_half8(pxl + o) : zero8;
             }
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < T; ++t)
-    #pragma unroll
+#pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int r = 4 * g + (lane >> 4), c = (lane & 15) ^ r;
                     stg[wv][0][t][r][c] = ga[t][g];
@@ -290,9 +290,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < T; ++t)
-    #pragma unroll
+#pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int c = (4 * s + q) ^ m;
                     const half8 wa_ = as_half8(stg[wv][0][t][m][c]);
@@ -312,9 +312,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
         __syncthreads();  // every wave is done with its slots before they hold sums
 
         // fixed-order sum over the waves: red[w][.][t][r*16 + n]
-    #pragma unroll
+#pragma unroll
         for (int t = 0; t < T; ++t)
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 red[wv][0][t][(4 * q + i) * 16 + m] = ca[t][i];
                 if constexpr (GATED) red[wv][NM - 1][t][(4 * q + i) * 16 + m] = cu[t][i];
