@@ -70,6 +70,7 @@ struct Ws {
     int32_t *idx, *count, *gcnt, *lst_i;
     _Float16 *xhi, *xlo, *hhi, *hlo, *ahi, *alo;
     uint16_t *tmask;
+    float *ss, *tsc;
     int ld_act;
     int chunks;
 };
@@ -98,6 +99,8 @@ Ws carve(const Layer &L, int B, void *ws) {
     w.ahi = reinterpret_cast<_Float16 *>(base + lo.ahi);
     w.alo = reinterpret_cast<_Float16 *>(base + lo.alo);
     w.tmask = reinterpret_cast<uint16_t *>(base + lo.tmask);
+    w.ss = reinterpret_cast<float *>(base + lo.ss);
+    w.tsc = reinterpret_cast<float *>(base + lo.tsc);
     w.ld_act = lo.ld_act;
     w.chunks = lo.chunks;
     return w;
@@ -125,10 +128,14 @@ bool single(const Layer &L, int B) { return B == 1 && b1_fits(L); }
 // split_ready: the batched path's fp16 split of x is already in w.xhi/xlo.
 // tiles: (matrix-core path) the rows are the union rows marked in w.tmask
 // instead of (idx, count); their list goes to w.idx / w.count (and count2).
+// raw: the split in w.xhi/xlo is of the raw residual stream; the products are
+// scaled by the RMS scale the predictor stored to w.tsc.  split_out: the
+// reduce also writes the split of y and its sums of squares (w.ss) for the
+// next layer.
 spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
                      const int32_t *idx, const int32_t *count, const float *resid, float *y,
                      const Ws &w, hipStream_t s, bool split_ready = false, bool tiles = false,
-                     int32_t *count2 = nullptr) {
+                     int32_t *count2 = nullptr, bool raw = false, bool split_out = false) {
     if (single(L, B)) {
         SPFFN_HIP(launch_up_b1(L, x, scale, idx, count, w.act, s), "gather up/gate launch");
         SPFFN_HIP(launch_down_b1(L, idx, count, w.act, w.part, w.chunks, s), "gather down launch");
@@ -140,17 +147,23 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
         if (!split_ready)
             SPFFN_HIP(launch_split_act(x, B, L.desc.d, 0.0f, false, nullptr, w.xhi, w.xlo, s),
                       "split launch");
+        const float *tsc = raw ? w.tsc : nullptr;
         if (tiles)
             SPFFN_HIP(launch_mfma_ffn_tiles(L, w.xhi, w.xlo, B, w.tmask, w.idx, w.count, count2,
-                                            w.ahi, w.alo, w.ld_act, w.part, s),
+                                            w.ahi, w.alo, w.ld_act, w.part, tsc, s),
                       "batched gather launch");
         else
             SPFFN_HIP(launch_mfma_ffn(L, w.xhi, w.xlo, B, idx, count, w.ahi, w.alo, w.ld_act,
-                                      w.part, s),
+                                      w.part, tsc, s),
                       "batched gather launch");
-        SPFFN_HIP(launch_reduce_groups(w.part, mfma_down_chunks(), (int64_t)B * L.desc.d, resid,
-                                       y, s),
-                  "reduce launch");
+        if (split_out)
+            SPFFN_HIP(launch_reduce_split(w.part, mfma_down_chunks(), B, L.desc.d, resid, y, w.xhi,
+                                          w.xlo, w.ss, s),
+                      "reduce launch");
+        else
+            SPFFN_HIP(launch_reduce_groups(w.part, mfma_down_chunks(), (int64_t)B * L.desc.d,
+                                           resid, y, s),
+                      "reduce launch");
         return SPFFN_OK;
     }
     SPFFN_HIP(launch_ffn_up(L, x, B, idx, count, w.act, s), "gather up/gate launch");
@@ -164,9 +177,12 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
 // Predictor of B tokens.  normalize: x is the residual stream and is RMS
 // normalised first (decode); the RMS scale goes to w.scale.  tiles: the
 // matrix-core path also writes the union bits per 16-row tile to w.tmask.
+// raw: (matrix-core path) w.xhi/xlo hold the split of the raw residual
+// stream and w.ss its sums of squares; the RMS scale is applied after layer
+// 1 and stored per token to w.tsc.
 spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, float eps,
                          float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s,
-                         bool split_ready = false, bool tiles = false) {
+                         bool split_ready = false, bool tiles = false, bool raw = false) {
     const spffn_layer_desc &D = L.desc;
     if (single(L, B)) {
         SPFFN_HIP(launch_w1_b1(L, x, eps, normalize, w.hid, w.scale, s), "predictor layer-1 launch");
@@ -181,7 +197,8 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
             SPFFN_HIP(launch_split_act(x, B, D.d, eps, normalize, w.n, w.xhi, w.xlo, s),
                       "split launch");
         SPFFN_HIP(launch_mfma_predict(L, w.xhi, w.xlo, B, w.w1p, w.hid, w.hhi, w.hlo, logits, mask,
-                                      uni, tiles ? w.tmask : nullptr, s),
+                                      uni, tiles ? w.tmask : nullptr, raw ? w.ss : nullptr, eps,
+                                      raw ? w.tsc : nullptr, s),
                   "batched predictor launch");
         return SPFFN_OK;
     }
@@ -207,6 +224,19 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     WsLayout lo{};
     lo.chunks = down_chunks(L);
     size_t off = 0;
+    // The batched decode hands these from layer to layer, so they come first:
+    // their offsets depend only on B and d, the same for every layer.
+    const bool mf = B > 1 && mfma_fits(L, B);
+    // packed B operands: 16 columns x K halves each (hi; lo for B > 8)
+    const size_t nx = mf ? (size_t)16 * D.d * 2 : 0;
+    lo.xhi = off;
+    off += up256(nx);
+    lo.xlo = off;
+    off += up256(nx);
+    lo.ss = off;
+    off += up256(mf ? (size_t)B * (D.d / 32) * 4 : 0);
+    lo.tsc = off;
+    off += up256(mf ? (size_t)B * 4 : 0);
     lo.n = off;
     off += up256((size_t)B * D.d * 4);
     lo.hid = off;
@@ -238,15 +268,9 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     lo.part = off;
     off += up256((size_t)lo.chunks * B * D.d * 4);
     // fp16 splits of the batched path (only when it applies)
-    const bool mf = B > 1 && mfma_fits(L, B);
     lo.ld_act = (D.d_ffn + 7) / 8 * 8;
-    // packed B operands: 16 columns x K halves each (hi; lo for B > 8)
-    const size_t nx = mf ? (size_t)16 * D.d * 2 : 0, nh = mf ? (size_t)16 * D.r * 2 : 0;
+    const size_t nh = mf ? (size_t)16 * D.r * 2 : 0;
     const size_t na = mf ? (size_t)B * lo.ld_act * 2 : 0;
-    lo.xhi = off;
-    off += up256(nx);
-    lo.xlo = off;
-    off += up256(nx);
     lo.hhi = off;
     off += up256(nh);
     lo.hlo = off;
@@ -578,6 +602,7 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
     }
     if (x != h) SPFFN_HIP(launch_copy_words(x, h, (int64_t)B * d, s), "input copy launch");
     size_t mask_off = 0, logit_off = 0;
+    bool split_ready = false;  // w.xhi/xlo/ss already hold this layer's input split
     for (size_t l = 0; l < model->layers.size(); ++l) {
         const Layer &L = model->layers[l]->L;
         const int F = L.desc.d_ffn;
@@ -593,15 +618,30 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         // (the matrix-core path also splits the normalised input into fp16 halves)
         const float *xin = one ? h : w.n;
         const bool mf = !one && mfma_fits(L, B);
-        if (mf)
+        // Matrix-core layers of a sparse step chain: each layer's reduce also
+        // writes the packed split of the raw h (and its sums of squares) that
+        // the next one multiplies; the RMS scale is applied after the products.
+        const bool chain = mf && !dense;
+        bool next_chain = false;
+        if (chain && l + 1 < model->layers.size()) {
+            const Layer &Ln = model->layers[l + 1]->L;
+            next_chain = !single(Ln, B) && mfma_fits(Ln, B);
+        }
+        if (chain) {
+            if (!split_ready)
+                SPFFN_HIP(launch_reduce_split(nullptr, 0, B, d, h, h, w.xhi, w.xlo, w.ss, s),
+                          "split launch");
+        } else if (mf) {
             SPFFN_HIP(launch_split_act(h, B, d, model->eps, true, w.n, w.xhi, w.xlo, s),
                       "rmsnorm launch");
-        else if (!one)
+        } else if (!one) {
             SPFFN_HIP(launch_rmsnorm(h, B, d, model->eps, w.n, s), "rmsnorm launch");
+        }
         if (!dense) {
             // the matrix-core gather lists the union rows itself (from tile
             // masks of the predictor's last kernel); other paths compact
-            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf, mf)))
+            if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf, mf,
+                                  chain)))
                 return st;
             if (!mf)
                 SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,
@@ -620,9 +660,10 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
         }
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l], s), "event record");
-        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s, mf, mf && !dense,
-                          layer_counts ? layer_counts + l : nullptr)))
+        if ((st = run_ffn(L, xin, one ? w.scale : nullptr, B, idx, cnt, h, h, w, s, mf, chain,
+                          layer_counts ? layer_counts + l : nullptr, chain, next_chain)))
             return st;
+        split_ready = next_chain;
         if (trace && trace->events)
             SPFFN_HIP(hipEventRecord((hipEvent_t)trace->events[2 * l + 1], s), "event record");
         mask_off += F;

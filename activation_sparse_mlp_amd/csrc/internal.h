@@ -35,6 +35,7 @@ struct WsLayout {
     size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, part, total;
     size_t xhi, xlo, hhi, hlo, ahi, alo, w1p;  // fp16 splits and partials of the batched path
     size_t tmask;                              // union bits per 16-row tile (batched path)
+    size_t ss, tsc;  // batched decode: sums of squares of h per 32 columns, RMS scale per token
     int ld_act;  // row pitch (elements) of ahi / alo
     int chunks;  // neuron chunks of the down projection (partial-sum slots)
 };
@@ -95,20 +96,28 @@ int mfma_down_chunks();
 int mfma_w1_splits();
 hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
                             _Float16 *hi, _Float16 *lo, hipStream_t s);
-// tmask (or nullptr): the union bits of each 16-row tile, for launch_mfma_ffn_tiles
+// tmask (or nullptr): the union bits of each 16-row tile, for launch_mfma_ffn_tiles.
+// ss (or nullptr): the input is the raw residual stream, with its sums of
+// squares per 32 columns (launch_reduce_split); the predictor then applies the
+// RMS scale and stores it per token to tsc.
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
                                float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
-                               hipStream_t s);
+                               const float *ss, float eps, float *tsc, hipStream_t s);
+// tsc (or nullptr): per-token scale of the products (the RMS scale of a raw input)
 hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                            const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
-                           int ld_act, float *part, hipStream_t s);
+                           int ld_act, float *part, const float *tsc, hipStream_t s);
 // The same over the union rows given by tile masks; the list is built on the
 // device and written to idx[0..*count) (and *count2 when given).
 hipError_t launch_mfma_ffn_tiles(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                  const uint16_t *tmask, int32_t *idx, int32_t *count,
                                  int32_t *count2, _Float16 *ahi, _Float16 *alo, int ld_act,
-                                 float *part, hipStream_t s);
+                                 float *part, const float *tsc, hipStream_t s);
+// y = resid + sum of chunks partial sums (chunks may be 0) over [B, d], plus the
+// packed fp16 split of y and its sums of squares per 32 columns (ss: B * d/32)
+hipError_t launch_reduce_split(const float *part, int chunks, int B, int d, const float *resid,
+                               float *y, _Float16 *hi, _Float16 *lo, float *ss, hipStream_t s);
 
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s);

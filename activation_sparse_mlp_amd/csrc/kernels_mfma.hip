@@ -150,6 +150,7 @@ struct BgArgs {
     uint16_t *tmask_out;   // mask: union bits of each 16-row tile, or nullptr
     _Float16 *ahi, *alo;   // act: [B, ld_act], entry j of the list
     int ld_act;
+    const float *tsc;      // act: per-token scale of the products (raw input), or nullptr
 };
 
 template <int WV, int T, bool GATED, bool SPLIT2, int EPI>
@@ -348,8 +349,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                 if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
                 if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
             } else {
-                float v = fmaxf(za + (a.bias ? a.bias[rr] : 0.0f), 0.0f);
-                if constexpr (GATED) v *= zu;
+                const float sc = a.tsc ? a.tsc[n] : 1.0f;
+                float v = fmaxf(fmaf(za, sc, a.bias ? a.bias[rr] : 0.0f), 0.0f);
+                if constexpr (GATED) v *= zu * sc;
                 const _Float16 h = (_Float16)v;
                 a.ahi[(size_t)n * a.ld_act + jj] = h;
                 a.alo[(size_t)n * a.ld_act + jj] = (_Float16)(v - (float)h);
@@ -376,21 +378,85 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
     }
 }
 
-// hid[b, i] = ReLU(sum over the K splits of part + b1[i]), fp32 and split
-// (packed B operand of predictor layer 2).
+// hid[b, i] = ReLU(s_b * (sum over the K splits of part) + b1[i]), fp32 and
+// split (packed B operand of predictor layer 2); block (x, b) takes rows
+// [256x, 256x + 256) of token b.  With ss (sums of x^2 over each 32-column
+// group of token b, nss of them) the input was the raw residual stream and
+// s_b = 1 / sqrt(mean(x^2) + eps) is its RMS scale (every block of the token
+// sums the same values in the same order; block 0 stores it to tsc[b]);
+// without it s_b = 1.
 __global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict__ part, int KS,
                                                         int B, int r, const float *__restrict__ b1,
+                                                        const float *__restrict__ ss, int nss,
+                                                        float inv_k, float eps,
                                                         float *__restrict__ hid,
                                                         _Float16 *__restrict__ hhi,
-                                                        _Float16 *__restrict__ hlo) {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= B * r) return;
-    const int i = t % r;
-    float v = 0.0f;
-    for (int c = 0; c < KS; ++c) v += part[(size_t)c * B * r + t];
-    v = fmaxf(v + (b1 ? b1[i] : 0.0f), 0.0f);
-    hid[t] = v;
-    bpack_store(hhi, hlo, B, t / r, i, v);
+                                                        _Float16 *__restrict__ hlo,
+                                                        float *__restrict__ tsc) {
+    __shared__ float red[4];
+    const int b = blockIdx.y;
+    float s = 1.0f;
+    if (ss) {
+        float q = 0.0f;
+        for (int i = threadIdx.x; i < nss; i += blockDim.x) q += ss[(size_t)b * nss + i];
+        q = wave_sum(q);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = q;
+        __syncthreads();
+        s = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) * inv_k + eps);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && tsc) tsc[b] = s;
+    }
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < r) {
+        const size_t t = (size_t)b * r + i;
+        float v = 0.0f;
+        for (int c = 0; c < KS; ++c) v += part[(size_t)c * B * r + t];
+        v = fmaxf(fmaf(v, s, b1 ? b1[i] : 0.0f), 0.0f);
+        hid[t] = v;
+        bpack_store(hhi, hlo, B, b, i, v);
+    }
+}
+
+// y = resid + sum_c part[c] over [B, d] (chunks may be 0), summed as
+// reduce_groups_kernel does, and in the same pass the packed fp16 split of y
+// (the next layer's B operand, not normalised) and the sum of y^2 over each
+// 32-column group, ss[b * d/32 + g], from which that layer takes its RMS scale.
+// One block per 32 consecutive elements of one token (d a multiple of 32).
+__global__ __launch_bounds__(256) void reduce_split_kernel(const float *__restrict__ part,
+                                                           int chunks, int B, int d,
+                                                           const float *resid, float *y,
+                                                           _Float16 *__restrict__ hi,
+                                                           _Float16 *__restrict__ lo,
+                                                           float *__restrict__ ss) {
+    __shared__ float red[8][33];
+    const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int64_t n = (int64_t)B * d;
+    const int64_t e = (int64_t)blockIdx.x * 32 + col;
+    float acc = 0.0f;
+    constexpr int V = 8;
+    for (int c0 = g; c0 < chunks; c0 += 8 * V) {
+        float v[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int cc = c0 + 8 * u;
+            v[u] = cc < chunks ? part[(int64_t)cc * n + e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u) acc += v[u];
+    }
+    red[g][col] = acc;
+    __syncthreads();
+    if (g == 0) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tot += red[k][col];
+        const float v = resid[e] + tot;
+        y[e] = v;
+        bpack_store(hi, lo, B, (int)(e / d), (int)(e % d), v);
+        float q = v * v;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
+        if (col == 0) ss[blockIdx.x] = q;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -570,6 +636,13 @@ bool mfma_fits(const Layer &L, int B) {
 int mfma_down_chunks() { return kBdChunks; }
 int mfma_w1_splits() { return kW1Splits; }
 
+hipError_t launch_reduce_split(const float *part, int chunks, int B, int d, const float *resid,
+                               float *y, _Float16 *hi, _Float16 *lo, float *ss, hipStream_t s) {
+    reduce_split_kernel<<<(int)((int64_t)B * d / 32), 256, 0, s>>>(part, chunks, B, d, resid, y, hi,
+                                                                   lo, ss);
+    return hipGetLastError();
+}
+
 hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,
                             _Float16 *hi, _Float16 *lo, hipStream_t s) {
     // K is a multiple of 4096 on this path, so the chunks are whole float4s
@@ -595,7 +668,7 @@ static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
                                float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
-                               hipStream_t s) {
+                               const float *ss, float eps, float *tsc, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     BgArgs a{};
     a.wa = reinterpret_cast<const _Float16 *>(L.w1.data);
@@ -606,8 +679,8 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     a.B = B;
     a.part = w1part;
     launch_bg<false, kEpiPartial, kBgWaves, kBgWaves>(a, dim3((D.r + 15) / 16, kW1Splits), s);
-    w1_finish_kernel<<<(B * D.r + 255) / 256, 256, 0, s>>>(w1part, kW1Splits, B, D.r, D.p_b1, hid,
-                                                          hhi, hlo);
+    w1_finish_kernel<<<dim3((D.r + 255) / 256, B), 256, 0, s>>>(
+        w1part, kW1Splits, B, D.r, D.p_b1, ss, D.d / 32, 1.0f / (float)D.d, eps, hid, hhi, hlo, tsc);
     BgArgs b{};
     b.wa = reinterpret_cast<const _Float16 *>(L.w2.data);
     b.K = D.r;
@@ -628,6 +701,7 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
 // gate/up products over the list, then the down projection into part
 static hipError_t mfma_ffn(const Layer &L, BgArgs a, dim3 grid, const int32_t *idx,
                            const int32_t *count, int B, float *part, hipStream_t s) {
+    // a.tsc (if set) scales the products per token
     const spffn_layer_desc &D = L.desc;
     const bool gated = D.kind == SPFFN_REGLU;
     a.wa = reinterpret_cast<const _Float16 *>((gated ? L.gate : L.up).data);
@@ -658,8 +732,9 @@ static hipError_t mfma_ffn(const Layer &L, BgArgs a, dim3 grid, const int32_t *i
 
 hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                            const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
-                           int ld_act, float *part, hipStream_t s) {
+                           int ld_act, float *part, const float *tsc, hipStream_t s) {
     BgArgs a{};
+    a.tsc = tsc;
     a.idx = idx;
     a.count = count;
     a.xhi = xhi;
@@ -673,8 +748,9 @@ hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *
 hipError_t launch_mfma_ffn_tiles(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                  const uint16_t *tmask, int32_t *idx, int32_t *count,
                                  int32_t *count2, _Float16 *ahi, _Float16 *alo, int ld_act,
-                                 float *part, hipStream_t s) {
+                                 float *part, const float *tsc, hipStream_t s) {
     BgArgs a{};
+    a.tsc = tsc;
     a.tmask = tmask;
     a.ntiles = (L.desc.d_ffn + 15) / 16;
     a.idx_out = idx;
