@@ -253,8 +253,8 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     off += up256((size_t)B * 4);
     lo.act = off;
     off += up256((size_t)B * D.d_ffn * 4);
-    const size_t G = (size_t)fused_groups(L), slots = G * fused_rows_per_group(L);
-    lo.gcnt = off;
+    const size_t G = (size_t)fused_groups(L), slots = fused_list_slots(L);
+    lo.gcnt = off;  // rows listed per down-projection chunk (chunks <= G)
     off += up256(G * 4);
     lo.lst_i = off;
     off += up256(slots * 4);
@@ -317,18 +317,18 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
             e0 = (hipEvent_t)trace->events[2 * l];
             e1 = (hipEvent_t)trace->events[2 * l + 1];
         }
-        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.gcnt, w.lst_i, w.lst_a, s,
-                                     e0, e1),
+        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, s, e0, e1),
                   "predictor layer-2 + gather launch");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
                                      s),
                       "trace copy");
         const int chunks = fused_chunks(L);
-        SPFFN_HIP(launch_down_list_b1(L, w.gcnt, w.lst_i, w.lst_a, w.part, chunks,
-                                      layer_counts ? layer_counts + l : nullptr, s),
+        int32_t *lc = layer_counts ? layer_counts + l : nullptr;
+        SPFFN_HIP(launch_down_list_b1(L, w.lst_i, w.lst_a, w.part, chunks, lc ? w.gcnt : nullptr,
+                                      s),
                   "gather down launch");
-        SPFFN_HIP(launch_reduce_groups(w.part, chunks, d, h, h, s), "reduce launch");
+        SPFFN_HIP(launch_reduce_groups(w.part, chunks, d, h, h, s, w.gcnt, lc), "reduce launch");
         mask_off += F;
         logit_off += F;
     }

@@ -119,8 +119,10 @@ hipError_t launch_mfma_ffn_tiles(const Layer &L, const _Float16 *xhi, const _Flo
 hipError_t launch_reduce_split(const float *part, int chunks, int B, int d, const float *resid,
                                float *y, _Float16 *hi, _Float16 *lo, float *ss, hipStream_t s);
 
+// y = resid + sum_c part[c]; optionally *total_out = sum of chunk_cnt[0..chunks)
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
-                                float *y, hipStream_t s);
+                                float *y, hipStream_t s, const int32_t *chunk_cnt = nullptr,
+                                int32_t *total_out = nullptr);
 
 // Fused predictor layer 2 + threshold + gate/up gather and its list-driven
 // down projection (decode, one token).
@@ -128,12 +130,13 @@ bool fused_fits(const Layer &L);
 int fused_groups(const Layer &L);
 int fused_rows_per_group(const Layer &L);
 int fused_chunks(const Layer &L);
+int fused_per_chunk(const Layer &L);
+size_t fused_list_slots(const Layer &L);  // list slots of the fused kernel (chunk-major)
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
-                              float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
-                              float *lst_a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                              float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
+                              hipStream_t s, hipEvent_t ev_start = nullptr,
                               hipEvent_t ev_stop = nullptr);
-hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t *lst_i,
-                               const float *lst_a, float *part, int chunks, int32_t *total_out,
-                               hipStream_t s);
+hipError_t launch_down_list_b1(const Layer &L, const int32_t *lst_i, const float *lst_a,
+                               float *part, int chunks, int32_t *chunk_cnt, hipStream_t s);
 
 }  // namespace spffn

@@ -358,7 +358,9 @@ __global__ __launch_bounds__(256) void down_b1_kernel(DownB1Args a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restrict__ part,
                                                             int chunks, int64_t n,
-                                                            const float *resid, float *y) {
+                                                            const float *resid, float *y,
+                                                            const int32_t *__restrict__ ccnt,
+                                                            int32_t *total_out) {
     __shared__ float red[8][33];
     const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
     const int64_t e = (int64_t)blockIdx.x * 32 + col;
@@ -384,6 +386,14 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
         for (int k = 0; k < 8; ++k) tot += red[k][col];
         y[e] = resid ? resid[e] + tot : tot;
     }
+    // optional: total of the per-chunk row counts (first wave of block 0)
+    if (total_out && blockIdx.x == 0 && threadIdx.x < 64) {
+        int c = 0;
+        for (int k = threadIdx.x; k < chunks; k += 64) c += ccnt[k];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+        if (threadIdx.x == 0) *total_out = c;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -393,9 +403,12 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
 // so the hot-first rows spread one per workgroup.  It computes their logits,
 // writes the mask, lists its active rows in LDS (ascending within the
 // workgroup), and then computes the activation of each listed row with all
-// four waves sharing the row's packets.  Output per workgroup g: cnt[g] and
-// the slots [g*RB, g*RB + cnt[g]) of lst_i / lst_a (neuron, activation).
-// Concatenated in workgroup order, the slots hold every active neuron once.
+// four waves sharing the row's packets.  Output per workgroup g: all RB
+// slots of its list in lst_i / lst_a (neuron, activation; its active rows
+// first, the rest neuron -1).  The lists are stored
+// chunk-major for the down projection: group g = c + C*j (C chunks) owns
+// slots [(c*NG + j)*RB, +RB) with NG = ceil(G / C), so the lists of one chunk
+// are contiguous and can be read without first reading the counts.
 // ---------------------------------------------------------------------------
 struct FusedArgs {
     WMat w2, wa, wu;
@@ -409,9 +422,10 @@ struct FusedArgs {
     const float *scale;   // device RMS scale
     float *logits;        // [d_ffn] or nullptr
     uint8_t *mask;        // [d_ffn]
-    int32_t *cnt;         // [G]
-    int32_t *lst_i;       // [G*RB]
-    float *lst_a;         // [G*RB]
+    int32_t *lst_i;       // [C*NG*RB]
+    float *lst_a;         // [C*NG*RB]
+    int chunks;           // C: chunks of the down projection
+    int per_chunk;        // NG = ceil(G / C): groups per chunk
 };
 
 template <int PF, int FMT, bool GATED, int RW, int UA>
@@ -549,43 +563,57 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
         }
     }
     __syncthreads();
-    if ((int)threadIdx.x < n_act) {
+    if ((int)threadIdx.x < RB) {
         const int k = threadIdx.x;
-        float vz = 0.0f, vu = 0.0f;
-        for (int w = 0; w < 4; ++w) {
-            vz += s_part[k][w][0];
-            vu += s_part[k][w][1];
+        int row = -1;
+        float v = 0.0f;
+        if (k < n_act) {
+            float vz = 0.0f, vu = 0.0f;
+            for (int w = 0; w < 4; ++w) {
+                vz += s_part[k][w][0];
+                vu += s_part[k][w][1];
+            }
+            v = fmaxf(fmaf(vz, s, s_bias[s_loc[k]]), 0.0f);
+            if constexpr (GATED) v *= vu * s;
+            row = s_list[k];
         }
-        float v = fmaxf(fmaf(vz, s, s_bias[s_loc[k]]), 0.0f);
-        if constexpr (GATED) v *= vu * s;
-        a.lst_i[g * RB + k] = s_list[k];
-        a.lst_a[g * RB + k] = v;
+        const size_t slot = ((size_t)(g % a.chunks) * a.per_chunk + g / a.chunks) * RB + k;
+        a.lst_i[slot] = row;
+        a.lst_a[slot] = v;
     }
-    if (threadIdx.x == 0) a.cnt[g] = n_act;
 }
 
 // ---------------------------------------------------------------------------
 // down projection over the per-workgroup lists of the fused kernel: block
 // (slice, chunk c) takes the lists of workgroups c, c + C, c + 2C, ... in that
 // order.  Striding (rather than contiguous ranges) spreads the hot-first rows,
-// which all sit in the first workgroups, evenly over the chunks.
+// which all sit in the first workgroups, evenly over the chunks.  The chunk's
+// slots are contiguous, so every thread requests its share of them at once;
+// the active ones (neuron >= 0) are compacted into LDS in slot order, and
+// wave w then takes rows w, w + 4, w + 8, ... of that list.
 // ---------------------------------------------------------------------------
 struct DownListArgs {
     WMat wd;
     int d, d_ffn;
-    const int32_t *cnt;
     const int32_t *lst_i;
     const float *lst_a;
     int G, RB;
     int chunks;
+    int per_chunk;         // groups per chunk (slot stride of a chunk: per_chunk * RB)
     float *part;           // [chunks, d]
-    int32_t *total_out;    // device int32 or nullptr: number of listed rows
+    int32_t *chunk_cnt;    // [chunks] rows listed per chunk, or nullptr
 };
+
+constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 64, rows per group <= 20
 
 template <int FMT, int UR>
 __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
     constexpr int E = PacketElems<FMT>::value;
+    constexpr int SPT = kDownListMaxSlots / 256;  // slots per thread
     __shared__ float red[64 * E];
+    __shared__ int s_i[kDownListMaxSlots];
+    __shared__ float s_a[kDownListMaxSlots];
+    __shared__ int s_wc[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, c = blockIdx.y;
     const int NP = a.d / E;
@@ -593,64 +621,71 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
     const bool pv = p < NP;
     const int C = a.chunks;
     const int ng = (a.G - c + C - 1) / C;  // groups c + C*j, j < ng; at most 64 (launcher)
+    const int S = ng * a.RB;                // slots of this chunk
+    const size_t base = (size_t)c * a.per_chunk * a.RB;
 
-    // per-lane count of group c + C*lane, then an inclusive scan over the wave
-    const int my_cnt = lane < ng ? a.cnt[c + C * lane] : 0;
-    int incl = my_cnt;
+    int vi[SPT];
+    float va[SPT];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
+    for (int u = 0; u < SPT; ++u) {
+        const int sl = (int)threadIdx.x + 256 * u;
+        vi[u] = sl < S ? a.lst_i[base + sl] : -1;
+        va[u] = sl < S ? a.lst_a[base + sl] : 0.0f;
     }
-    const int T = __shfl(incl, 63, 64);  // rows in this chunk
-    if (a.total_out && slice == 0 && wv == 0) {
-        // whole-layer count: sum of every workgroup's count (block (0, 0) only)
-        if (c == 0) {
-            int tot = 0;
-            for (int gg = lane; gg < a.G; gg += 64) tot += a.cnt[gg];
+    // compaction of the active slots, in slot order
+    int T = 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-            if (lane == 0) *a.total_out = tot;
+    for (int u = 0; u < SPT; ++u) {
+        if (256 * u >= S) break;  // block-uniform
+        const bool act = vi[u] >= 0 && vi[u] < a.d_ffn;
+        const unsigned long long bal = __ballot(act);
+        if (lane == 0) s_wc[wv] = __popcll(bal);
+        __syncthreads();
+        int at = T;
+        for (int w = 0; w < wv; ++w) at += s_wc[w];
+        if (act) {
+            const int q = at + __popcll(bal & below);
+            s_i[q] = vi[u];
+            s_a[q] = va[u];
         }
+        T += s_wc[0] + s_wc[1] + s_wc[2] + s_wc[3];
+        __syncthreads();
     }
+    if (a.chunk_cnt && slice == 0 && threadIdx.x == 0) a.chunk_cnt[c] = T;
 
     float acc[E], corr = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
-    for (int fb = wv; fb < T; fb += 4 * 64) {
-        // lane l fetches flattened row f = fb + 4l
-        const int f = fb + 4 * lane;
-        // workgroup of f: the number of workgroups whose inclusive count is <= f
-        // (shuffles run on every lane; only lanes with f < T use the result)
-        int seg = 0;
-        for (int q = 0; q < ng; ++q) seg += (__shfl(incl, q, 64) <= f) ? 1 : 0;
-        const int prev = __shfl(incl, seg > 0 ? seg - 1 : 0, 64);
-        const int before = seg > 0 ? prev : 0;
-        int my_i = -1;
-        float my_a = 0.0f;
-        if (f < T && seg < ng) {
-            const int slot = (c + C * seg) * a.RB + (f - before);
-            my_i = a.lst_i[slot];
-            my_a = a.lst_a[slot];
-            if (my_i < 0 || my_i >= a.d_ffn) my_i = -1;
-        }
-        const int nk = min(64, (T - fb + 3) / 4);
-        for (int k0 = 0; k0 < nk; k0 += UR) {
-            uint4 raw[UR];
-            float sc[UR], av[UR];
+    for (int fb = wv; fb < T; fb += 4 * UR) {
+        // the batch's list entries first (clamped, so the LDS reads carry no
+        // branches), then all of its row loads
+        int ri[UR];
+        float av[UR];
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int ri = __shfl(my_i, k0 + u, 64);
-                av[u] = __shfl(my_a, k0 + u, 64);
-                const bool ok = (k0 + u < nk) && ri >= 0 && pv;
-                raw[u] = ok ? ld_stream(row_ptr<FMT>(a.wd, ri, a.d) + p) : make_uint4(0, 0, 0, 0);
-                sc[u] = ok ? packet_scale<FMT>(a.wd, ri, a.d, p) : 0.0f;
-                if (!ok) av[u] = 0.0f;
+        for (int u = 0; u < UR; ++u) {
+            const int f = fb + 4 * u;
+            const int fc = f < T ? f : T - 1;
+            ri[u] = s_i[fc];
+            av[u] = s_a[fc];
+        }
+        uint4 raw[UR];
+        float sc[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const bool ok = fb + 4 * u < T && pv;
+            raw[u] = make_uint4(0, 0, 0, 0);
+            sc[u] = 0.0f;
+            if (ok) {
+                raw[u] = ld_stream(row_ptr<FMT>(a.wd, ri[u], a.d) + p);
+                sc[u] = packet_scale<FMT>(a.wd, ri[u], a.d, p);
+            } else {
+                av[u] = 0.0f;
             }
-#pragma unroll
-            for (int u = 0; u < UR; ++u) packet_axpy<FMT>(raw[u], sc[u], av[u], acc, corr);
         }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) packet_axpy<FMT>(raw[u], sc[u], av[u], acc, corr);
     }
 
     packet_axpy_finish<FMT>(acc, corr);
@@ -789,6 +824,8 @@ constexpr int kFusedRW = 2;
 // (measured at the 175B-shaped layer: 8 rows 55.5 us, 12 rows 51.4, 16 rows
 // 50.4-51.2, 20 rows 48.0-48.7, 24 rows 55.2, 28 rows 49.7, 32 rows 52.4).
 constexpr int kFusedRWQ4 = 5;
+static_assert(4 * kFusedRW * 64 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 64 <= kDownListMaxSlots,
+              "a down-projection chunk must hold its groups' list slots");
 
 template <int FMT> constexpr int fused_rw() { return FMT == kQ4 ? kFusedRWQ4 : kFusedRW; }
 
@@ -807,6 +844,15 @@ int fused_chunks(const Layer &L) {
     int c = (G + 63) / 64;
     if (c < 64) c = 64;
     return c < G ? c : G;
+}
+
+int fused_per_chunk(const Layer &L) {
+    const int C = fused_chunks(L);
+    return (fused_groups(L) + C - 1) / C;
+}
+
+size_t fused_list_slots(const Layer &L) {
+    return (size_t)fused_chunks(L) * fused_per_chunk(L) * fused_rows_per_group(L);
 }
 
 // Activated-row packets per lane: one pass of 256*UA packets covers a row.
@@ -850,9 +896,8 @@ static void launch_fused_kind(const FusedArgs &a, bool gated, int G, int UA, hip
 }
 
 hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
-                              float *logits, uint8_t *mask, int32_t *cnt, int32_t *lst_i,
-                              float *lst_a, hipStream_t s, hipEvent_t ev_start,
-                              hipEvent_t ev_stop) {
+                              float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
+                              hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
     FusedArgs a{};
     const bool gated = D.kind == SPFFN_REGLU;
@@ -870,11 +915,12 @@ hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, 
     a.scale = scale;
     a.logits = logits;
     a.mask = mask;
-    a.cnt = cnt;
     a.lst_i = lst_i;
     a.lst_a = lst_a;
     const int G = fused_groups(L), UA = fused_ua(L);
     a.groups = G;
+    a.chunks = fused_chunks(L);
+    a.per_chunk = fused_per_chunk(L);
     if (D.p_dtype == SPFFN_F16) {
         if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF16, kF16>(a, gated, G, UA, s, ev_start, ev_stop);
         else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF16, kF32>(a, gated, G, UA, s, ev_start, ev_stop);
@@ -887,22 +933,23 @@ hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, 
     return hipGetLastError();
 }
 
-hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t *lst_i,
-                               const float *lst_a, float *part, int chunks, int32_t *total_out,
-                               hipStream_t s) {
+hipError_t launch_down_list_b1(const Layer &L, const int32_t *lst_i, const float *lst_a,
+                               float *part, int chunks, int32_t *chunk_cnt, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
+    // the fused kernel laid its lists out for exactly fused_chunks(L) chunks
+    if (chunks != fused_chunks(L)) return hipErrorInvalidValue;
     DownListArgs a{};
     a.wd = L.down;
     a.d = D.d;
     a.d_ffn = D.d_ffn;
-    a.cnt = cnt;
     a.lst_i = lst_i;
     a.lst_a = lst_a;
     a.G = fused_groups(L);
     a.RB = fused_rows_per_group(L);
     a.chunks = chunks;
+    a.per_chunk = fused_per_chunk(L);
     a.part = part;
-    a.total_out = total_out;
+    a.chunk_cnt = chunk_cnt;
     const int E = packet_elems(D.w_dtype);
     dim3 grid((D.d / E + 63) / 64, chunks);
     switch (D.w_dtype) {
@@ -914,8 +961,10 @@ hipError_t launch_down_list_b1(const Layer &L, const int32_t *cnt, const int32_t
 }
 
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
-                                float *y, hipStream_t s) {
-    reduce_groups_kernel<<<(int)((n + 31) / 32), 256, 0, s>>>(part, chunks, n, resid, y);
+                                float *y, hipStream_t s, const int32_t *chunk_cnt,
+                                int32_t *total_out) {
+    reduce_groups_kernel<<<(int)((n + 31) / 32), 256, 0, s>>>(part, chunks, n, resid, y, chunk_cnt,
+                                                              total_out);
     return hipGetLastError();
 }
 
