@@ -521,6 +521,8 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
     // (wv, lane) always takes packets wv*64 + lane + 256u, so its activation
     // values are loaded once, into registers, after the first row's weights
     // have been requested (a group without active rows never reads them)
+    // Packets past the end of a row load a clamped (valid) packet and meet
+    // zero activation values, so every load is unconditional.
     float xv[UA][E], xs[UA];
     for (int k = 0; k < n_act; ++k) {
         const int i = s_list[k];
@@ -529,15 +531,12 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
 #pragma unroll
         for (int u = 0; u < UA; ++u) {
             const int p = wv * 64 + lane + 256 * u;
-            const bool ok = p < NPd;
-            const int pc = ok ? p : NPd - 1;
-            const uint4 va = ld_stream(row_ptr<FMT>(a.wa, i, a.d) + pc);
-            ra[u] = ok ? va : make_uint4(0, 0, 0, 0);
-            sa[u] = ok ? packet_scale<FMT>(a.wa, i, a.d, pc) : 0.0f;
+            const int pc = p < NPd ? p : NPd - 1;
+            ra[u] = ld_stream(row_ptr<FMT>(a.wa, i, a.d) + pc);
+            sa[u] = packet_scale<FMT>(a.wa, i, a.d, pc);
             if constexpr (GATED) {
-                const uint4 vu = ld_stream(row_ptr<FMT>(a.wu, i, a.d) + pc);
-                ru[u] = ok ? vu : make_uint4(0, 0, 0, 0);
-                su[u] = ok ? packet_scale<FMT>(a.wu, i, a.d, pc) : 0.0f;
+                ru[u] = ld_stream(row_ptr<FMT>(a.wu, i, a.d) + pc);
+                su[u] = packet_scale<FMT>(a.wu, i, a.d, pc);
             }
         }
         if (k == 0) {
@@ -547,13 +546,25 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
                 load_packet_x<FMT>(a.h, p < NPd ? p : NPd - 1, xv[u], xs[u]);
             }
         }
+        // keep every load of the row ahead of the first use (the scheduler
+        // otherwise issues one load, waits for it, then issues the rest)
+        __builtin_amdgcn_sched_barrier(0);
+        if (k == 0) {
+#pragma unroll
+            for (int u = 0; u < UA; ++u)
+                if (wv * 64 + lane + 256 * u >= NPd) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) xv[u][e] = 0.0f;
+                    xs[u] = 0.0f;
+                }
+        }
+        // no bounds branch here: out-of-range packets have zero activations,
+        // and a branch lets the compiler sink their loads behind a full wait
         float za = 0.0f, zu = 0.0f;
 #pragma unroll
         for (int u = 0; u < UA; ++u) {
-            if (wv * 64 + lane + 256 * u < NPd) {
-                za = packet_dot_reg<FMT>(ra[u], sa[u], xv[u], xs[u], za);
-                if constexpr (GATED) zu = packet_dot_reg<FMT>(ru[u], su[u], xv[u], xs[u], zu);
-            }
+            za = packet_dot_reg<FMT>(ra[u], sa[u], xv[u], xs[u], za);
+            if constexpr (GATED) zu = packet_dot_reg<FMT>(ru[u], su[u], xv[u], xs[u], zu);
         }
         za = wave_sum(za);
         if constexpr (GATED) zu = wave_sum(zu);
