@@ -67,7 +67,7 @@ WMat wmat(const void *p, int dtype, int rows, int cols) {
 struct Ws {
     float *n, *hid, *act, *part, *scale, *lst_a, *w1p;
     uint8_t *mask, *uni;
-    int32_t *idx, *count, *gcnt, *lst_i;
+    int32_t *idx, *count, *gcnt, *lst_i, *done;
     _Float16 *xhi, *xlo, *hhi, *hlo, *ahi, *alo;
     uint16_t *tmask;
     float *ss, *tsc;
@@ -90,6 +90,7 @@ Ws carve(const Layer &L, int B, void *ws) {
     w.gcnt = reinterpret_cast<int32_t *>(base + lo.gcnt);
     w.lst_i = reinterpret_cast<int32_t *>(base + lo.lst_i);
     w.lst_a = reinterpret_cast<float *>(base + lo.lst_a);
+    w.done = reinterpret_cast<int32_t *>(base + lo.done);
     w.part = reinterpret_cast<float *>(base + lo.part);
     w.w1p = reinterpret_cast<float *>(base + lo.w1p);
     w.xhi = reinterpret_cast<_Float16 *>(base + lo.xhi);
@@ -260,6 +261,8 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     off += up256(slots * 4);
     lo.lst_a = off;
     off += up256(slots * 4);
+    lo.done = off;  // row groups published per down-projection chunk (single token)
+    off += up256((size_t)fused_chunks(L) * kFusedDoneStride * 4);
     if (B == 1 && b1_fits(L)) {
         lo.chunks = down_b1_chunks(L);
         if (fused_fits(L) && fused_chunks(L) > lo.chunks) lo.chunks = fused_chunks(L);
@@ -291,17 +294,25 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
 
 namespace {
 
-// One-token decode through a uniform stack, four kernels per layer:
+// One-token decode through a uniform stack, three kernels per layer:
 //   1. predictor layer 1, which also yields the RMS scale of h;
 //   2. predictor layer 2 + threshold + gate/up gather + activation, with
-//      per-workgroup lists of the active neurons;
-//   3. the down projection over those lists into per-chunk partial sums;
-//   4. the fixed-order reduction of the partial sums with the residual add.
+//      per-group lists of the active neurons, and in the same launch the down
+//      projection over those lists into per-chunk partial sums (each chunk
+//      starts as soon as its groups have published their lists);
+//   3. the fixed-order reduction of the partial sums with the residual add,
+//      which also clears the chunk counters for the next layer.
 spffn_status decode_one_token(const spffn_model *model, const float *x, float *h,
                               int32_t *layer_counts, const spffn_trace *trace, void *ws,
                               hipStream_t s) {
     const int d = model->d;
     if (x != h) SPFFN_HIP(launch_copy_words(x, h, d, s), "input copy launch");
+    {
+        // the workspace comes uninitialised: clear the chunk counters once
+        const Layer &L0 = model->layers[0]->L;
+        SPFFN_HIP(launch_fill_i32(carve(L0, 1, ws).done, 0, fused_chunks(L0) * kFusedDoneStride, s),
+                  "counter clear launch");
+    }
     size_t mask_off = 0, logit_off = 0;
     for (size_t l = 0; l < model->layers.size(); ++l) {
         const Layer &L = model->layers[l]->L;
@@ -317,18 +328,19 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
             e0 = (hipEvent_t)trace->events[2 * l];
             e1 = (hipEvent_t)trace->events[2 * l + 1];
         }
-        SPFFN_HIP(launch_pred2_up_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, s, e0, e1),
-                  "predictor layer-2 + gather launch");
+        const int chunks = fused_chunks(L);
+        int32_t *lc = layer_counts ? layer_counts + l : nullptr;
+        SPFFN_HIP(launch_layer_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, w.done, w.part,
+                                  lc ? w.gcnt : nullptr, s, e0, e1),
+                  "predictor layer-2 + gather + down launch");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
                                      s),
                       "trace copy");
-        const int chunks = fused_chunks(L);
-        int32_t *lc = layer_counts ? layer_counts + l : nullptr;
-        SPFFN_HIP(launch_down_list_b1(L, w.lst_i, w.lst_a, w.part, chunks, lc ? w.gcnt : nullptr,
-                                      s),
-                  "gather down launch");
-        SPFFN_HIP(launch_reduce_groups(w.part, chunks, d, h, h, s, w.gcnt, lc), "reduce launch");
+        // the reduce also clears the chunk counters for the next layer
+        SPFFN_HIP(launch_reduce_groups(w.part, chunks, d, h, h, s, w.gcnt, lc, w.done, chunks,
+                                       kFusedDoneStride),
+                  "reduce launch");
         mask_off += F;
         logit_off += F;
     }

@@ -32,7 +32,7 @@ struct Layer {
 
 // Workspace carve-up for a batch of B tokens.
 struct WsLayout {
-    size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, part, total;
+    size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, done, part, total;
     size_t xhi, xlo, hhi, hlo, ahi, alo, w1p;  // fp16 splits and partials of the batched path
     size_t tmask;                              // union bits per 16-row tile (batched path)
     size_t ss, tsc;  // batched decode: sums of squares of h per 32 columns, RMS scale per token
@@ -120,9 +120,11 @@ hipError_t launch_reduce_split(const float *part, int chunks, int B, int d, cons
                                float *y, _Float16 *hi, _Float16 *lo, float *ss, hipStream_t s);
 
 // y = resid + sum_c part[c]; optionally *total_out = sum of chunk_cnt[0..chunks)
+// and zero[k * zero_stride] = 0 for k < n_zero
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s, const int32_t *chunk_cnt = nullptr,
-                                int32_t *total_out = nullptr);
+                                int32_t *total_out = nullptr, int32_t *zero = nullptr,
+                                int n_zero = 0, int zero_stride = 1);
 
 // Fused predictor layer 2 + threshold + gate/up gather and its list-driven
 // down projection (decode, one token).
@@ -132,11 +134,14 @@ int fused_rows_per_group(const Layer &L);
 int fused_chunks(const Layer &L);
 int fused_per_chunk(const Layer &L);
 size_t fused_list_slots(const Layer &L);  // list slots of the fused kernel (chunk-major)
-hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
-                              float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
-                              hipStream_t s, hipEvent_t ev_start = nullptr,
-                              hipEvent_t ev_stop = nullptr);
-hipError_t launch_down_list_b1(const Layer &L, const int32_t *lst_i, const float *lst_a,
-                               float *part, int chunks, int32_t *chunk_cnt, hipStream_t s);
+// Predictor layer 2 + threshold + gate/up gather + down projection of one
+// layer (single token) in one launch.  done holds fused_chunks(L) counters,
+// kFusedDoneStride words apart, which must be zero (the whole region may be
+// cleared).
+constexpr int kFusedDoneStride = 1024;
+hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
+                           float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
+                           int32_t *done, float *part, int32_t *chunk_cnt, hipStream_t s,
+                           hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace spffn

@@ -360,7 +360,8 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
                                                             int chunks, int64_t n,
                                                             const float *resid, float *y,
                                                             const int32_t *__restrict__ ccnt,
-                                                            int32_t *total_out) {
+                                                            int32_t *total_out, int32_t *zero,
+                                                            int n_zero, int zero_stride) {
     __shared__ float red[8][33];
     const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
     const int64_t e = (int64_t)blockIdx.x * 32 + col;
@@ -394,22 +395,41 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
         for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
         if (threadIdx.x == 0) *total_out = c;
     }
+    if (blockIdx.x == 0)
+        for (int k = threadIdx.x; k < n_zero; k += blockDim.x) zero[(size_t)k * zero_stride] = 0;
 }
 
 // ---------------------------------------------------------------------------
-// fused predictor layer 2 + threshold + gate/up gather (decode, one token)
+// One layer of the single-token decode after predictor layer 1, in one
+// launch: G row-group workgroups (predictor layer 2 + threshold + gate/up
+// gather) followed by C*S down-projection workgroups (S column slices per
+// chunk of NG consecutive row groups).
 //
-// Workgroup g owns the interleaved W2 rows {g + G*k : k < RB} (G workgroups),
-// so the hot-first rows spread one per workgroup.  It computes their logits,
-// writes the mask, lists its active rows in LDS (ascending within the
-// workgroup), and then computes the activation of each listed row with all
-// four waves sharing the row's packets.  Output per workgroup g: all RB
-// slots of its list in lst_i / lst_a (neuron, activation; its active rows
-// first, the rest neuron -1).  The lists are stored
-// chunk-major for the down projection: group g = c + C*j (C chunks) owns
-// slots [(c*NG + j)*RB, +RB) with NG = ceil(G / C), so the lists of one chunk
-// are contiguous and can be read without first reading the counts.
+// Row group g owns the interleaved W2 rows {g + G*k : k < RB}, so the
+// hot-first rows spread one per group.  It computes their logits, writes the
+// mask, lists its active rows in LDS (ascending within the group), computes
+// the activation of each listed row with all four waves sharing the row's
+// packets, and writes the RB slots [g*RB, g*RB + RB) of lst_i / lst_a
+// (neuron, activation; its active rows first, the rest neuron -1).  It then
+// publishes them: the slots are written with agent-scope (L2-coherent)
+// stores, and once they have completed, done[c] of its chunk c = g / NG is
+// incremented.
+//
+// A down-projection workgroup (chunk c, slice) waits until done[c] counts
+// every group of its chunk, then reads the chunk's slots (contiguous, with
+// agent-scope loads) and accumulates its column slice.  Its workgroup index is above every row
+// group's, so every group it waits for was dispatched before it and never
+// waits itself; the wait is also bounded, and a workgroup that runs out of
+// patience writes NaN partial sums instead of hanging.  Chunks are ranges of
+// consecutive groups, so the chunks of the first groups (which hold the
+// hottest rows) are complete first and the down projection overlaps the
+// tail of the gather.
 // ---------------------------------------------------------------------------
+// Chunk counters sit 4 KB apart: atomics and polls on one memory line
+// serialise, and 64 counters packed into two lines cost tens of microseconds
+// per layer.
+constexpr int kDoneStride = kFusedDoneStride;
+
 struct FusedArgs {
     WMat w2, wa, wu;
     int d, d_ffn, r;
@@ -422,14 +442,14 @@ struct FusedArgs {
     const float *scale;   // device RMS scale
     float *logits;        // [d_ffn] or nullptr
     uint8_t *mask;        // [d_ffn]
-    int32_t *lst_i;       // [C*NG*RB]
-    float *lst_a;         // [C*NG*RB]
-    int chunks;           // C: chunks of the down projection
-    int per_chunk;        // NG = ceil(G / C): groups per chunk
+    int32_t *lst_i;       // [G*RB]
+    float *lst_a;         // [G*RB]
+    int per_chunk;        // NG: consecutive groups per down-projection chunk
+    int32_t *done;        // [C * kDoneStride] groups published per chunk (zero at launch)
 };
 
 template <int PF, int FMT, bool GATED, int RW, int UA>
-__global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
+__device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
     constexpr int RB = 4 * RW;     // rows per row group (one group per workgroup)
@@ -440,7 +460,7 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
     __shared__ float s_bias[RB];   // bias of every row of the group, by local index
     __shared__ float s_part[RB][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int G = a.groups, g = blockIdx.x;
+    const int G = a.groups;
     const int NPr = a.r / EP, NPd = a.d / E;
 
     // Everything the W2 phase needs is requested up front, straight into
@@ -588,20 +608,31 @@ __global__ __launch_bounds__(256) void pred2_up_b1_kernel(FusedArgs a) {
             if constexpr (GATED) v *= vu * s;
             row = s_list[k];
         }
-        const size_t slot = ((size_t)(g % a.chunks) * a.per_chunk + g / a.chunks) * RB + k;
-        a.lst_i[slot] = row;
-        a.lst_a[slot] = v;
+        // agent-scope stores: coherent across the chip's L2 caches by
+        // themselves, so publishing needs no cache write-back
+        __hip_atomic_store(a.lst_i + (size_t)g * RB + k, row, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.lst_a + (size_t)g * RB + k, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // publish the list: the slots were written by lanes of wave 0 only; that
+    // wave waits until its stores have completed, then counts the group in
+    // (a release fence would also write back the whole L2, which costs far
+    // more than the wait when every group does it)
+    if (wv == 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (lane == 0)
+            __hip_atomic_fetch_add(a.done + (size_t)(g / a.per_chunk) * kDoneStride, 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---------------------------------------------------------------------------
-// down projection over the per-workgroup lists of the fused kernel: block
-// (slice, chunk c) takes the lists of workgroups c, c + C, c + 2C, ... in that
-// order.  Striding (rather than contiguous ranges) spreads the hot-first rows,
-// which all sit in the first workgroups, evenly over the chunks.  The chunk's
-// slots are contiguous, so every thread requests its share of them at once;
-// the active ones (neuron >= 0) are compacted into LDS in slot order, and
-// wave w then takes rows w, w + 4, w + 8, ... of that list.
+// down projection of one chunk's lists, one column slice: every thread
+// requests its share of the chunk's slots at once, the active ones
+// (neuron >= 0) are compacted into LDS in slot order, and wave w then takes
+// rows w, w + 4, w + 8, ... of that list.
 // ---------------------------------------------------------------------------
 struct DownListArgs {
     WMat wd;
@@ -610,7 +641,7 @@ struct DownListArgs {
     const float *lst_a;
     int G, RB;
     int chunks;
-    int per_chunk;         // groups per chunk (slot stride of a chunk: per_chunk * RB)
+    int per_chunk;         // consecutive groups per chunk
     float *part;           // [chunks, d]
     int32_t *chunk_cnt;    // [chunks] rows listed per chunk, or nullptr
 };
@@ -618,7 +649,8 @@ struct DownListArgs {
 constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 64, rows per group <= 20
 
 template <int FMT, int UR>
-__global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
+__device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slice, const int c,
+                                           const bool ready) {
     constexpr int E = PacketElems<FMT>::value;
     constexpr int SPT = kDownListMaxSlots / 256;  // slots per thread
     __shared__ float red[64 * E];
@@ -626,22 +658,33 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
     __shared__ float s_a[kDownListMaxSlots];
     __shared__ int s_wc[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int slice = blockIdx.x, c = blockIdx.y;
     const int NP = a.d / E;
     const int p = slice * 64 + lane;
     const bool pv = p < NP;
-    const int C = a.chunks;
-    const int ng = (a.G - c + C - 1) / C;  // groups c + C*j, j < ng; at most 64 (launcher)
-    const int S = ng * a.RB;                // slots of this chunk
-    const size_t base = (size_t)c * a.per_chunk * a.RB;
+    const int g0 = c * a.per_chunk;
+    const int ng = min(a.per_chunk, a.G - g0);  // groups of this chunk, at most 64 (launcher)
+    const int S = ng * a.RB;                     // slots of this chunk
+    const size_t base = (size_t)g0 * a.RB;
+    const int col0 = slice * 64 * E;
+    if (!ready) {
+        // the chunk's lists never arrived: poison the partial sums
+        for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
+            if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = __builtin_nanf("");
+        return;
+    }
 
     int vi[SPT];
     float va[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
+        // agent-scope loads: they see the row groups' agent-scope stores
         const int sl = (int)threadIdx.x + 256 * u;
-        vi[u] = sl < S ? a.lst_i[base + sl] : -1;
-        va[u] = sl < S ? a.lst_a[base + sl] : 0.0f;
+        vi[u] = sl < S ? __hip_atomic_load(a.lst_i + base + sl, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : -1;
+        va[u] = sl < S ? __hip_atomic_load(a.lst_a + base + sl, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.0f;
     }
     // compaction of the active slots, in slot order
     int T = 0;
@@ -710,9 +753,49 @@ __global__ __launch_bounds__(256) void down_list_b1_kernel(DownListArgs a) {
         }
         __syncthreads();
     }
-    const int col0 = slice * 64 * E;
     for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
         if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = red[t];
+}
+
+// Polls before a down-projection workgroup gives up on its chunk (each poll
+// is an atomic read at agent scope plus a short sleep; far beyond any layer's
+// run time).
+constexpr int kChunkWaitPolls = 1 << 18;
+
+// Five resident waves per SIMD where the registers allow it without spills
+// (wider rows and gated 4-bit rows keep the compiler's own budget).
+template <int FMT, bool GATED, int UA>
+constexpr int layer_b1_waves() {
+    return (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
+}
+
+template <int PF, int FMT, bool GATED, int RW, int UA, int UR>
+__global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer_b1_kernel(
+    FusedArgs f, DownListArgs dn, int slices) {
+    if ((int)blockIdx.x < f.groups) {
+        fused_group<PF, FMT, GATED, RW, UA>(f, blockIdx.x);
+        return;
+    }
+    const int q = (int)blockIdx.x - f.groups;
+    const int c = q / slices, slice = q - c * slices;
+    const int need = min(dn.per_chunk, dn.G - c * dn.per_chunk);
+    __shared__ int s_ready;
+    if (threadIdx.x == 0) {
+        int ok = 0;
+        for (int it = 0; it < kChunkWaitPolls; ++it) {
+            if (__hip_atomic_load(f.done + (size_t)c * kDoneStride, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) >= need) {
+                ok = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s_ready = ok;
+    }
+    // every wave issues its slot loads after this barrier, so after the count
+    // was seen complete
+    __syncthreads();
+    down_chunk<FMT, UR>(dn, slice, c, s_ready != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,22 +931,29 @@ int fused_groups(const Layer &L) {
     return (L.desc.d_ffn + RB - 1) / RB;
 }
 
-// Down-projection row chunks over the fused kernel's lists: at most 64 groups
-// per chunk (one wave scans their counts), at least 64 chunks.
-int fused_chunks(const Layer &L) {
+// Down-projection chunks: ranges of NG consecutive row groups, NG <= 64 (so a
+// chunk's slots fit the down workgroup's LDS list), at least 64 chunks when
+// there are that many groups.
+int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
     int c = (G + 63) / 64;
     if (c < 64) c = 64;
-    return c < G ? c : G;
+    if (c > G) c = G;
+    return (G + c - 1) / c;
 }
 
-int fused_per_chunk(const Layer &L) {
-    const int C = fused_chunks(L);
-    return (fused_groups(L) + C - 1) / C;
+int fused_chunks(const Layer &L) {
+    const int NG = fused_per_chunk(L);
+    return (fused_groups(L) + NG - 1) / NG;
 }
 
 size_t fused_list_slots(const Layer &L) {
-    return (size_t)fused_chunks(L) * fused_per_chunk(L) * fused_rows_per_group(L);
+    return (size_t)fused_groups(L) * fused_rows_per_group(L);
+}
+
+// Column slices of the down projection: 64 packets each.
+static int down_slices(const Layer &L) {
+    return (L.desc.d / packet_elems(L.desc.w_dtype) + 63) / 64;
 }
 
 // Activated-row packets per lane: one pass of 256*UA packets covers a row.
@@ -880,102 +970,99 @@ bool fused_fits(const Layer &L) {
 }
 
 template <int PF, int FMT, bool GATED, int RW, int UA>
-static void launch_fused_t(const FusedArgs &a, int G, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+static void launch_layer_t(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
+                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int UR = FMT == kQ4 ? 8 : 16;
     // with timing events the dispatch itself is timestamped (the events bracket
     // the kernel's execution, not its launch)
     if (e0 || e1)
-        hipExtLaunchKernelGGL(pred2_up_b1_kernel<PF, FMT, GATED, RW, UA>, dim3(G), dim3(256), 0, s,
-                              e0, e1, 0, a);
+        hipExtLaunchKernelGGL(layer_b1_kernel<PF, FMT, GATED, RW, UA, UR>, dim3(blocks), dim3(256), 0,
+                              s, e0, e1, 0, f, dn, slices);
     else
-        pred2_up_b1_kernel<PF, FMT, GATED, RW, UA><<<G, 256, 0, s>>>(a);
+        layer_b1_kernel<PF, FMT, GATED, RW, UA, UR><<<blocks, 256, 0, s>>>(f, dn, slices);
 }
 
 template <int PF, int FMT, bool GATED>
-static void launch_fused_rw(const FusedArgs &a, int G, int UA, hipStream_t s, hipEvent_t e0,
-                            hipEvent_t e1) {
+static void launch_layer_rw(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
+                            int UA, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int RW = fused_rw<FMT>();
-    if (UA == 2) launch_fused_t<PF, FMT, GATED, RW, 2>(a, G, s, e0, e1);
-    else if (UA == 4) launch_fused_t<PF, FMT, GATED, RW, 4>(a, G, s, e0, e1);
-    else launch_fused_t<PF, FMT, GATED, RW, 8>(a, G, s, e0, e1);
+    if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2>(f, dn, slices, blocks, s, e0, e1);
+    else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4>(f, dn, slices, blocks, s, e0, e1);
+    else launch_layer_t<PF, FMT, GATED, RW, 8>(f, dn, slices, blocks, s, e0, e1);
 }
 
 template <int PF, int FMT>
-static void launch_fused_kind(const FusedArgs &a, bool gated, int G, int UA, hipStream_t s,
-                              hipEvent_t e0, hipEvent_t e1) {
-    if (gated) launch_fused_rw<PF, FMT, true>(a, G, UA, s, e0, e1);
-    else launch_fused_rw<PF, FMT, false>(a, G, UA, s, e0, e1);
+static void launch_layer_kind(const FusedArgs &f, const DownListArgs &dn, bool gated, int slices,
+                              int blocks, int UA, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (gated) launch_layer_rw<PF, FMT, true>(f, dn, slices, blocks, UA, s, e0, e1);
+    else launch_layer_rw<PF, FMT, false>(f, dn, slices, blocks, UA, s, e0, e1);
 }
 
-hipError_t launch_pred2_up_b1(const Layer &L, const float *hid, const float *h, const float *scale,
-                              float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
-                              hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
+                           float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
+                           int32_t *done, float *part, int32_t *chunk_cnt, hipStream_t s,
+                           hipEvent_t ev_start, hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
-    FusedArgs a{};
     const bool gated = D.kind == SPFFN_REGLU;
-    a.w2 = L.w2;
-    a.wa = gated ? L.gate : L.up;
-    a.wu = L.up;
-    a.d = D.d;
-    a.d_ffn = D.d_ffn;
-    a.r = D.r;
-    a.hid = hid;
-    a.b2 = D.p_b2;
-    a.t = L.t;
-    a.bias = D.b_act;
-    a.h = h;
-    a.scale = scale;
-    a.logits = logits;
-    a.mask = mask;
-    a.lst_i = lst_i;
-    a.lst_a = lst_a;
-    const int G = fused_groups(L), UA = fused_ua(L);
-    a.groups = G;
-    a.chunks = fused_chunks(L);
-    a.per_chunk = fused_per_chunk(L);
+    const int G = fused_groups(L), UA = fused_ua(L), C = fused_chunks(L), NG = fused_per_chunk(L);
+    const int slices = down_slices(L);
+    FusedArgs f{};
+    f.w2 = L.w2;
+    f.wa = gated ? L.gate : L.up;
+    f.wu = L.up;
+    f.d = D.d;
+    f.d_ffn = D.d_ffn;
+    f.r = D.r;
+    f.groups = G;
+    f.hid = hid;
+    f.b2 = D.p_b2;
+    f.t = L.t;
+    f.bias = D.b_act;
+    f.h = h;
+    f.scale = scale;
+    f.logits = logits;
+    f.mask = mask;
+    f.lst_i = lst_i;
+    f.lst_a = lst_a;
+    f.per_chunk = NG;
+    f.done = done;
+    DownListArgs dn{};
+    dn.wd = L.down;
+    dn.d = D.d;
+    dn.d_ffn = D.d_ffn;
+    dn.lst_i = lst_i;
+    dn.lst_a = lst_a;
+    dn.G = G;
+    dn.RB = fused_rows_per_group(L);
+    dn.chunks = C;
+    dn.per_chunk = NG;
+    dn.part = part;
+    dn.chunk_cnt = chunk_cnt;
+    const int blocks = G + C * slices;
     if (D.p_dtype == SPFFN_F16) {
-        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF16, kF16>(a, gated, G, UA, s, ev_start, ev_stop);
-        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF16, kF32>(a, gated, G, UA, s, ev_start, ev_stop);
-        else launch_fused_kind<kF16, kQ4>(a, gated, G, UA, s, ev_start, ev_stop);
+        if (D.w_dtype == SPFFN_F16)
+            launch_layer_kind<kF16, kF16>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32)
+            launch_layer_kind<kF16, kF32>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else
+            launch_layer_kind<kF16, kQ4>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
     } else {
-        if (D.w_dtype == SPFFN_F16) launch_fused_kind<kF32, kF16>(a, gated, G, UA, s, ev_start, ev_stop);
-        else if (D.w_dtype == SPFFN_F32) launch_fused_kind<kF32, kF32>(a, gated, G, UA, s, ev_start, ev_stop);
-        else launch_fused_kind<kF32, kQ4>(a, gated, G, UA, s, ev_start, ev_stop);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_down_list_b1(const Layer &L, const int32_t *lst_i, const float *lst_a,
-                               float *part, int chunks, int32_t *chunk_cnt, hipStream_t s) {
-    const spffn_layer_desc &D = L.desc;
-    // the fused kernel laid its lists out for exactly fused_chunks(L) chunks
-    if (chunks != fused_chunks(L)) return hipErrorInvalidValue;
-    DownListArgs a{};
-    a.wd = L.down;
-    a.d = D.d;
-    a.d_ffn = D.d_ffn;
-    a.lst_i = lst_i;
-    a.lst_a = lst_a;
-    a.G = fused_groups(L);
-    a.RB = fused_rows_per_group(L);
-    a.chunks = chunks;
-    a.per_chunk = fused_per_chunk(L);
-    a.part = part;
-    a.chunk_cnt = chunk_cnt;
-    const int E = packet_elems(D.w_dtype);
-    dim3 grid((D.d / E + 63) / 64, chunks);
-    switch (D.w_dtype) {
-        case SPFFN_F32: down_list_b1_kernel<kF32, 16><<<grid, 256, 0, s>>>(a); break;
-        case SPFFN_F16: down_list_b1_kernel<kF16, 16><<<grid, 256, 0, s>>>(a); break;
-        default: down_list_b1_kernel<kQ4, 8><<<grid, 256, 0, s>>>(a); break;
+        if (D.w_dtype == SPFFN_F16)
+            launch_layer_kind<kF32, kF16>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32)
+            launch_layer_kind<kF32, kF32>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else
+            launch_layer_kind<kF32, kQ4>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s, const int32_t *chunk_cnt,
-                                int32_t *total_out) {
+                                int32_t *total_out, int32_t *zero, int n_zero,
+                                int zero_stride) {
     reduce_groups_kernel<<<(int)((n + 31) / 32), 256, 0, s>>>(part, chunks, n, resid, y, chunk_cnt,
-                                                              total_out);
+                                                              total_out, zero, n_zero, zero_stride);
     return hipGetLastError();
 }
 
