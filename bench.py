@@ -25,7 +25,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 # HBM bytes per launch of the dominant kernel, measured with the profiler's
 # FETCH_SIZE / WRITE_SIZE counters (scaled by a plain copy of known size) and
 # stored with a hash of the kernel's sources; used only while they still match.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "pred2_up_b1_llama2_70b_b1_traffic.md")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "layer_b1_llama2_70b_b1_traffic.md")
 KERNEL_SOURCES = ["activation_sparse_mlp_amd/csrc/kernels_b1.hip",
                   "activation_sparse_mlp_amd/csrc/device.h",
                   "activation_sparse_mlp_amd/csrc/internal.h"]
@@ -92,15 +92,17 @@ def step_bytes(layers, counts, B):
 
 
 def dominant_kernel_bytes(L, u, B):
-    """Algorithmic bytes of one launch of the kernel that streams predictor
-    layer 2 and gathers the gate/up rows (single token): every W2 row and its
-    bias, the mask byte of every neuron, and for each of the u active neurons
-    its activated rows (gate and up, or up), its bias and its list entry
-    (index + activation), plus the hidden and residual vectors read."""
+    """Algorithmic bytes of one launch of the single-token layer kernel, which
+    streams predictor layer 2, gathers the gate/up rows and runs the down
+    projection: every W2 row and its bias, the mask byte of every neuron, and
+    for each of the u active neurons its rows of every FFN matrix (gate, up and
+    down, or up and down), its bias and its list entry (index + activation),
+    plus the hidden and residual vectors read.  The per-chunk partial sums it
+    writes are workspace traffic, not counted."""
     wp = 4 if L.p_dtype == "f32" else 2
     row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
-    n_act = 2 if L.kind == "reglu" else 1
-    return (L.d_ffn * (L.r * wp + 4 + 1) + int(u) * (n_act * row + 4 + 8)
+    n_mat = 3 if L.kind == "reglu" else 2
+    return (L.d_ffn * (L.r * wp + 4 + 1) + int(u) * (n_mat * row + 4 + 8)
             + B * (L.r + L.d) * 4)
 
 
@@ -291,9 +293,10 @@ def main():
 
     # ---- the dominant kernel, timed live with HIP events ------------------- #
     # A second timed pass of the same steps records an event pair around each
-    # layer's largest kernel: the predictor layer-2 + gate/up gather kernel at
-    # batch 1 (every workload here takes the fused single-token path), the
-    # batched FFN kernels otherwise.  The headline pass carries no events.
+    # layer's largest kernel: the single-token layer kernel (predictor layer 2,
+    # gate/up gather and down projection in one launch) at batch 1 (every
+    # workload here takes that path), the batched FFN kernels otherwise.  The
+    # headline pass carries no events.
     KE = max(1, min(K, 16))
     ev = HipEvents(2 * nl * KE)
     torch.cuda.synchronize()
@@ -313,7 +316,8 @@ def main():
     ev.close()
     kern_us = 1e3 * float(np.mean(k_ms))
     kern_gbs = float(np.mean(k_bytes)) / (kern_us * 1e-6) / 1e9
-    kern_name = ("predictor layer-2 + threshold + gate/up gather (one launch per layer)"
+    kern_name = ("predictor layer-2 + threshold + gate/up gather + down projection "
+                 "(one launch per layer)"
                  if B == 1 else "batched FFN: gate/up gather, down projection, reduce (per layer)")
     log(f"[kernel] {kern_name}: {kern_us:.2f} us/launch  {kern_gbs:.0f} GB/s "
         f"({len(k_ms)} launches)")

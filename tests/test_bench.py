@@ -42,11 +42,12 @@ def test_step_bytes_by_hand():
 
 def test_dominant_kernel_bytes_by_hand():
     # every W2 row + bias + mask byte: 32 * (4*2 + 4 + 1); 5 active rows of
-    # gate + up (2 * 16 bytes) + bias + list entry; hid and h read once
+    # gate + up + down (3 * 16 bytes) + bias + list entry; hid and h read once
     assert bench.dominant_kernel_bytes(_layer(), 5, 1) == \
-        32 * 13 + 5 * (2 * 16 + 4 + 8) + (4 + 8) * 4
+        32 * 13 + 5 * (3 * 16 + 4 + 8) + (4 + 8) * 4
+    # ReLU: up + down rows of 8 fp32 values
     assert bench.dominant_kernel_bytes(_layer(kind="relu", w_dtype="f32"), 2, 1) == \
-        32 * 13 + 2 * (32 + 4 + 8) + (4 + 8) * 4
+        32 * 13 + 2 * (2 * 32 + 4 + 8) + (4 + 8) * 4
 
 
 def test_batched_ffn_bytes_by_hand():
