@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
     const int64_t e = (int64_t)blockIdx.x * 32 + col;
     float s = 0.0f;
     if (e < n) {
-        constexpr int V = 8;
+        constexpr int V = 16;
         for (int c0 = g; c0 < chunks; c0 += 8 * V) {
             float v[V];
 #pragma unroll
