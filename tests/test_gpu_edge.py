@@ -1,5 +1,6 @@
 """Edge cases of the decode step on the GPU: a neuron count that leaves the
-single-token kernel's last row group partly empty, and the two degenerate
+single-token kernel's last row group partly empty, one that fills its
+down-projection chunks to capacity with a ragged last chunk, and the two degenerate
 predictors -- every neuron active (the step equals the dense step) and none
 active (the residual passes through unchanged, bit for bit)."""
 from dataclasses import replace
@@ -31,6 +32,14 @@ def _ragged(kind):
 def test_decode_ragged_row_groups(kind, B):
     print(f"edge decode ragged {kind} B={B}", flush=True)
     _decode_checks(_ragged(kind), B, 2, seed=51)
+
+
+def test_decode_most_groups_per_chunk():
+    # d_ffn = 65603: 8201 row groups of 8, so the single-token layer kernel uses
+    # 129 down-projection chunks of 64 groups (the most a chunk's list holds)
+    # and a last chunk of 9 groups
+    print("edge decode 8201 row groups", flush=True)
+    _decode_checks(replace(_ragged("relu"), d_ffn=65603), 1, 2, seed=53)
 
 
 def _model(cfg, tau, layers=2):
