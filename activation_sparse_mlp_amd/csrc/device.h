@@ -12,6 +12,8 @@
 // (xsum[b * NP + p]), so a block's dot product is  s * (sum q_k x_k - 8 sum x_k).
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace spffn {
@@ -63,10 +65,23 @@ __device__ __forceinline__ uint32_t and_word(uint32_t w, uint32_t mask) {
     return r;
 }
 
+// Sum over the 64 lanes, returned to every lane: within each row of 16 lanes
+// by DPP exchanges (pairs, quads, half-row and row mirrors; register-to-register,
+// no LDS round trip), then the four row sums in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                          0xF, 0xF, false));
+    };
+    v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    const int iv = __float_as_int(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
 }
 
 // Stage tokens x[b][c0 .. c0 + NP*E) for b < NB (zeros for b >= B) into LDS.

@@ -508,7 +508,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         for (int u = 0; u < PL; ++u)
             if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
         const float v = wave_sum(acc);
-        const float bq = __shfl(b2v, q, 64);
+        const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v), q));
         const int row = g + G * (wv + 4 * q);
         if (row < a.d_ffn) {
             const float l = v + bq;
