@@ -455,8 +455,6 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int RB = 4 * RW;     // rows per row group (one group per workgroup)
     constexpr int PL = 2;          // W2 packets per lane per row (rows of <= 128 packets)
     __shared__ uint32_t s_bits[4];
-    __shared__ int s_list[RB];     // listed rows, ascending
-    __shared__ int s_loc[RB];      // their local index k in the group
     __shared__ float s_bias[RB];   // bias of every row of the group, by local index
     __shared__ float s_part[RB][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -520,22 +518,20 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
             }
         }
     }
-    // list of the group's active rows, ordered by local index k = wv + 4q
-    // (ascending row g + G*k)
+    // the group's active rows as one mask over the local index k = wv + 4q
+    // (ascending k is ascending row g + G*k), built by every thread from the
+    // four waves' bits
     if (lane == 0) s_bits[wv] = bits;
     __syncthreads();
-    int n_act = 0;
-    for (int w = 0; w < 4; ++w) n_act += __popc(s_bits[w]);
-    if (threadIdx.x < RB) {
-        const int k = threadIdx.x, wk = k & 3, qk = k >> 2;
-        if ((s_bits[wk] >> qk) & 1u) {
-            int rank = 0;
-            for (int k2 = 0; k2 < k; ++k2) rank += (s_bits[k2 & 3] >> (k2 >> 2)) & 1u;
-            s_list[rank] = g + G * k;
-            s_loc[rank] = k;
-        }
+    uint32_t act_mask = 0;
+    {
+        const uint32_t b0 = s_bits[0], b1 = s_bits[1], b2 = s_bits[2], b3 = s_bits[3];
+#pragma unroll
+        for (int q = 0; q < RW; ++q)
+            act_mask |= (((b0 >> q) & 1u) << (4 * q)) | (((b1 >> q) & 1u) << (4 * q + 1)) |
+                        (((b2 >> q) & 1u) << (4 * q + 2)) | (((b3 >> q) & 1u) << (4 * q + 3));
     }
-    __syncthreads();
+    const int n_act = __popc(act_mask);
 
     // activations of the listed rows: the four waves share each row, lane
     // (wv, lane) always takes packets wv*64 + lane + 256u, so its activation
@@ -544,8 +540,11 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     // Packets past the end of a row load a clamped (valid) packet and meet
     // zero activation values, so every load is unconditional.
     float xv[UA][E], xs[UA];
+    uint32_t pending = act_mask;
     for (int k = 0; k < n_act; ++k) {
-        const int i = s_list[k];
+        const int kl = __ffs(pending) - 1;  // local index of the k-th active row
+        pending &= pending - 1;
+        const int i = g + G * kl;
         uint4 ra[UA], ru[UA];
         float sa[UA], su[UA];
 #pragma unroll
@@ -604,9 +603,13 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
                 vz += s_part[k][w][0];
                 vu += s_part[k][w][1];
             }
-            v = fmaxf(fmaf(vz, s, s_bias[s_loc[k]]), 0.0f);
+            // local index of the k-th active row
+            uint32_t m = act_mask;
+            for (int j = 0; j < k; ++j) m &= m - 1;
+            const int kl = __ffs(m) - 1;
+            v = fmaxf(fmaf(vz, s, s_bias[kl]), 0.0f);
             if constexpr (GATED) v *= vu * s;
-            row = s_list[k];
+            row = g + G * kl;
         }
         // agent-scope stores: coherent across the chip's L2 caches by
         // themselves, so publishing needs no cache write-back
@@ -653,7 +656,7 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
                                            const bool ready) {
     constexpr int E = PacketElems<FMT>::value;
     constexpr int SPT = kDownListMaxSlots / 256;  // slots per thread
-    __shared__ float red[64 * E];
+    __shared__ float red[4 * 64 * E <= kDownListMaxSlots ? 1 : 64 * E];
     __shared__ int s_i[kDownListMaxSlots];
     __shared__ float s_a[kDownListMaxSlots];
     __shared__ int s_wc[4];
@@ -743,18 +746,33 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
     }
 
     packet_axpy_finish<FMT>(acc, corr);
-    for (int w = 0; w < 4; ++w) {
-        if (wv == w) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float &rr = red[lane * E + e];
-                rr = (w == 0) ? acc[e] : rr + acc[e];
-            }
-        }
+    if constexpr (4 * 64 * E <= kDownListMaxSlots) {
+        // every wave parks its sums in a region of its own (the list's LDS,
+        // free once all waves are past their loads), then the four regions
+        // are added in wave order: two barriers instead of a chain of four
+        float *wr = reinterpret_cast<float *>(s_i);
         __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) wr[(wv * 64 + lane) * E + e] = acc[e];
+        __syncthreads();
+        for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
+            if (col0 + t < a.d)
+                a.part[(size_t)c * a.d + col0 + t] =
+                    ((wr[t] + wr[64 * E + t]) + wr[2 * 64 * E + t]) + wr[3 * 64 * E + t];
+    } else {
+        for (int w = 0; w < 4; ++w) {
+            if (wv == w) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float &rr = red[lane * E + e];
+                    rr = (w == 0) ? acc[e] : rr + acc[e];
+                }
+            }
+            __syncthreads();
+        }
+        for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
+            if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = red[t];
     }
-    for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
-        if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = red[t];
 }
 
 // Polls before a down-projection workgroup gives up on its chunk (each poll
