@@ -133,7 +133,7 @@ int fused_groups(const Layer &L);
 int fused_rows_per_group(const Layer &L);
 int fused_chunks(const Layer &L);
 int fused_per_chunk(const Layer &L);
-size_t fused_list_slots(const Layer &L);  // list slots of the fused kernel (chunk-major)
+size_t fused_list_slots(const Layer &L);  // list slots of the layer kernel (RB per row group)
 // Predictor layer 2 + threshold + gate/up gather + down projection of one
 // layer (single token) in one launch.  done holds fused_chunks(L) counters,
 // kFusedDoneStride words apart, which must be zero (the whole region may be

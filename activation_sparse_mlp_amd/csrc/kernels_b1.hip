@@ -2,12 +2,13 @@
 // issues its weight loads before anything that waits (LDS staging, the
 // normalisation, barriers), so the 128-bit streaming loads overlap them.
 //
-// Decode step, per layer (four kernels):
+// Decode step, per layer (three kernels):
 //   w1_b1        hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps)
-//   pred2_up_b1  logit = W2 . hid + b2, mask = logit > t, and for the active
-//                rows of each 8-row group act = max(z, 0) [* u] with
-//                z = (W_act[i] . h) * s + b_i, listed per group
-//   down_list_b1 part[c, slice] = sum over the lists of chunk c of
+//   layer_b1     row groups: logit = W2 . hid + b2, mask = logit > t, and for
+//                the active rows of each 8-row group act = max(z, 0) [* u]
+//                with z = (W_act[i] . h) * s + b_i, listed per group;
+//                down workgroups (same launch, once a chunk's groups are
+//                done): part[c, slice] = sum over the lists of chunk c of
 //                act * W_down_t[i, slice]
 //   reduce_groups h = h + sum_c part[c]
 // Single calls (spffn_predict / spffn_forward at one token): w1_b1, w2_b1
@@ -925,7 +926,7 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-// Row groups of the fused kernel: 8 rows per workgroup (two W2 rows per
+// Row groups of the layer kernel: 8 rows per workgroup (two W2 rows per
 // wave).  Small groups keep the kernel at 4-5 resident workgroups per CU and
 // let the hardware hand new groups to CUs whose groups had few active rows,
 // which balances the gather phase better than larger groups.

@@ -116,9 +116,10 @@ typedef struct spffn_model spffn_model; /* [host] opaque: an ordered layer stack
  * concatenated; logits [sum_l B * d_ffn_l]: each layer's predictor logits
  * [B, d_ffn_l]; events [2 L]: hipEvent_t handles (owned by the caller)
  * that time each layer's largest kernel: on the single-token path the kernel
- * streaming predictor layer 2 and gathering the gate/up rows, whose dispatch
- * is timestamped into events 2l (start) and 2l+1 (end); on other paths the
- * events are recorded on the stream around the FFN kernels. */
+ * that streams predictor layer 2, gathers the gate/up rows and runs the down
+ * projection, whose dispatch is timestamped into events 2l (start) and 2l+1
+ * (end); on other paths the events are recorded on the stream around the FFN
+ * kernels. */
 typedef struct {
     float *h_in;
     uint8_t *union_mask;

@@ -301,7 +301,7 @@ def test_q4_0_forward_and_predict(B):
 
 
 def test_q4_0_decode_b1_ragged_groups():
-    """Single-token decode with 4-bit rows (fused kernel, 20-row groups): 1530
+    """Single-token decode with 4-bit rows (layer kernel, 20-row groups): 1530
     neurons leave the last group half empty."""
     cfg = replace(OPT_175B_Q4, d=512, d_ffn=1530, r=64, layers=2)
     _decode_checks(cfg, 1, 2, seed=29)
