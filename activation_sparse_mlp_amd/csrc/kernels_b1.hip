@@ -926,24 +926,34 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-// Row groups of the layer kernel: 8 rows per workgroup (two W2 rows per
-// wave).  Small groups keep the kernel at 4-5 resident workgroups per CU and
+// Row groups of the layer kernel: 8 rows per workgroup for gated rows (two
+// W2 rows per wave).  Small groups keep the kernel at 4-5 resident workgroups per CU and
 // let the hardware hand new groups to CUs whose groups had few active rows,
 // which balances the gather phase better than larger groups.
 constexpr int kFusedRW = 2;
+// Non-gated rows gather one matrix per active row, so a group's gather is half
+// as long and larger groups (12 rows) spread the W2 phase better (measured at
+// the 40B-shaped ReLU stack: 8 rows 2.652 ms per step, 12 rows 2.574, 16
+// rows 2.695; at the gated 7B and 70B shapes 8 rows stay best).
+constexpr int kFusedRWNonGated = 3;
 // 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
 // row still reads the whole fp32 activation vector (and its block sums), so
 // their groups are larger (20 rows) to spread that read over more active rows
 // (measured at the 175B-shaped layer: 8 rows 55.5 us, 12 rows 51.4, 16 rows
 // 50.4-51.2, 20 rows 48.0-48.7, 24 rows 55.2, 28 rows 49.7, 32 rows 52.4).
 constexpr int kFusedRWQ4 = 5;
-static_assert(4 * kFusedRW * 64 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 64 <= kDownListMaxSlots,
+static_assert(4 * kFusedRW * 64 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 64 <= kDownListMaxSlots &&
+                  4 * kFusedRWNonGated * 64 <= kDownListMaxSlots,
               "a down-projection chunk must hold its groups' list slots");
 
-template <int FMT> constexpr int fused_rw() { return FMT == kQ4 ? kFusedRWQ4 : kFusedRW; }
+template <int FMT, bool GATED> constexpr int fused_rw() {
+    return FMT == kQ4 ? kFusedRWQ4 : GATED ? kFusedRW : kFusedRWNonGated;
+}
 
 int fused_rows_per_group(const Layer &L) {
-    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4 : kFusedRW);
+    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4
+                : L.desc.kind == SPFFN_REGLU  ? kFusedRW
+                                              : kFusedRWNonGated);
 }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
@@ -1006,7 +1016,7 @@ static void launch_layer_t(const FusedArgs &f, const DownListArgs &dn, int slice
 template <int PF, int FMT, bool GATED>
 static void launch_layer_rw(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
                             int UA, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr int RW = fused_rw<FMT>();
+    constexpr int RW = fused_rw<FMT, GATED>();
     if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2>(f, dn, slices, blocks, s, e0, e1);
     else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4>(f, dn, slices, blocks, s, e0, e1);
     else launch_layer_t<PF, FMT, GATED, RW, 8>(f, dn, slices, blocks, s, e0, e1);
