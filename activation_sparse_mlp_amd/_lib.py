@@ -67,6 +67,7 @@ SIGNATURES = {
     "spffn_hot_first_order": (_i32, [_vp, _i32, _vp, _vp]),
     "spffn_permute_rows": (_i32, [_vp, _vp, _vp, _i32, _i64, _vp]),
     "spffn_q4_0_repack": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "spffn_set_wait_limit": (_i32, [_i32]),
     "spffn_last_error": (C.c_char_p, []),
     "spffn_version": (C.c_char_p, []),
 }
@@ -118,6 +119,16 @@ def _dev(t, dtype, name):
 
 def version():
     return load().spffn_version().decode()
+
+
+WAIT_LIMIT_DEFAULT = 1 << 18
+
+
+def set_wait_limit(polls):
+    """Test hook: polls before a down-projection workgroup of the single-token
+    decode gives up on its chunk (NaN output instead of a hang); 0 makes it
+    give up at once.  Applies to launches enqueued afterwards."""
+    _check(load().spffn_set_wait_limit(int(polls)), "spffn_set_wait_limit")
 
 
 class Layer:

@@ -362,6 +362,14 @@ const char *spffn_last_error(void) { return g_err.c_str(); }
 
 const char *spffn_version(void) { return "spffn 0.1 (gfx950)"; }
 
+spffn_status spffn_set_wait_limit(int32_t polls) {
+    if (polls < 0 || polls > kChunkWaitPollsMax)
+        return fail(SPFFN_E_ARG, "set_wait_limit: polls=%d outside [0, %d]", polls,
+                    kChunkWaitPollsMax);
+    set_chunk_wait_polls(polls);
+    return SPFFN_OK;
+}
+
 spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out) {
     if (!desc || !out) return fail(SPFFN_E_ARG, "layer_create: NULL desc or out");
     const spffn_layer_desc &D = *desc;

@@ -139,6 +139,10 @@ size_t fused_list_slots(const Layer &L);  // list slots of the layer kernel (RB 
 // kFusedDoneStride words apart, which must be zero (the whole region may be
 // cleared).
 constexpr int kFusedDoneStride = 1024;
+// Bounded wait of the layer kernel's down-projection workgroups (polls).
+constexpr int kChunkWaitPollsDefault = 1 << 18;
+constexpr int kChunkWaitPollsMax = 1 << 24;
+void set_chunk_wait_polls(int polls);
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
                            int32_t *done, float *part, int32_t *chunk_cnt, hipStream_t s,

@@ -18,6 +18,8 @@
 // the vector first, up to rounding.)
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "device.h"
 
 namespace spffn {
@@ -648,6 +650,7 @@ struct DownListArgs {
     int per_chunk;         // consecutive groups per chunk
     float *part;           // [chunks, d]
     int32_t *chunk_cnt;    // [chunks] rows listed per chunk, or nullptr
+    int wait_polls;        // polls before giving up on a chunk
 };
 
 constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 64, rows per group <= 20
@@ -777,9 +780,11 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
 }
 
 // Polls before a down-projection workgroup gives up on its chunk (each poll
-// is an atomic read at agent scope plus a short sleep; far beyond any layer's
-// run time).
-constexpr int kChunkWaitPolls = 1 << 18;
+// is an atomic read at agent scope plus a short sleep; the default is far
+// beyond any layer's run time).  Process-wide, read when a launch is enqueued.
+static std::atomic<int> g_chunk_wait_polls{kChunkWaitPollsDefault};
+
+void set_chunk_wait_polls(int polls) { g_chunk_wait_polls.store(polls); }
 
 // Five resident waves per SIMD where the registers allow it without spills
 // (wider rows and gated 4-bit rows keep the compiler's own budget).
@@ -801,7 +806,7 @@ __global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer
     __shared__ int s_ready;
     if (threadIdx.x == 0) {
         int ok = 0;
-        for (int it = 0; it < kChunkWaitPolls; ++it) {
+        for (int it = 0; it < dn.wait_polls; ++it) {
             if (__hip_atomic_load(f.done + (size_t)c * kDoneStride, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT) >= need) {
                 ok = 1;
@@ -1069,6 +1074,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     dn.per_chunk = NG;
     dn.part = part;
     dn.chunk_cnt = chunk_cnt;
+    dn.wait_polls = g_chunk_wait_polls.load();
     const int blocks = G + C * slices;
     if (D.p_dtype == SPFFN_F16) {
         if (D.w_dtype == SPFFN_F16)

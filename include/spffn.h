@@ -265,6 +265,18 @@ spffn_status spffn_permute_rows(const void *src, void *dst, const int32_t *perm,
 spffn_status spffn_q4_0_repack(const void *aos, void *soa, int32_t rows, int32_t cols,
                                void *stream);
 
+/* [host] Test hook.  Inside the single-token decode step, the workgroups that
+ * run a chunk's down projection wait (in the same launch) until the row groups
+ * of that chunk have published their lists; the wait always ends, because
+ * those row groups were dispatched before them and never wait, and it is also
+ * bounded: after `polls` polls (default 2^18, far beyond any layer's run time)
+ * the workgroup gives up and writes NaN partial sums, so the step yields NaN
+ * instead of hanging.  polls in [0, 2^24]; 0 makes every such workgroup give
+ * up at once (for testing the give-up path).  Process-wide; applies to
+ * launches enqueued after the call (a captured graph keeps the value it was
+ * captured with).  SPFFN_E_ARG outside the range. */
+spffn_status spffn_set_wait_limit(int32_t polls);
+
 /* [host] Text of the calling thread's last non-OK status ("" if none). */
 const char *spffn_last_error(void);
 

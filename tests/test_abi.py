@@ -176,3 +176,14 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(TypeError):
         spffn.threshold(torch.zeros(4), 0.0)
+
+
+def test_set_wait_limit_range():
+    # host-side check only (no kernel runs): the bounded-wait test hook takes
+    # 0 .. 2^24 polls and rejects anything else before it takes effect
+    lib = spffn.load()
+    assert lib.spffn_set_wait_limit(-1) == E_ARG
+    assert lib.spffn_set_wait_limit((1 << 24) + 1) == E_ARG
+    assert lib.spffn_set_wait_limit(0) == OK
+    assert lib.spffn_set_wait_limit(1 << 24) == OK
+    assert lib.spffn_set_wait_limit(spffn.WAIT_LIMIT_DEFAULT) == OK

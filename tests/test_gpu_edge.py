@@ -42,6 +42,28 @@ def test_decode_most_groups_per_chunk():
     _decode_checks(replace(_ragged("relu"), d_ffn=65603), 1, 2, seed=53)
 
 
+def test_layer_kernel_wait_gives_up_with_nan():
+    # the single-token layer kernel's down-projection workgroups wait (bounded)
+    # for their chunk's row groups; with a limit of 0 polls every one of them
+    # gives up at once, and the step must complete with NaN rather than hang
+    cfg = _ragged("relu")
+    model = _model(cfg, tau=0.5)
+    x = make_tokens(cfg.d, 1, 1, seed=5, device=DEV)[0]
+    ref = spffn.decode_step(model, x)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    try:
+        spffn.set_wait_limit(0)
+        h = spffn.decode_step(model, x)
+        torch.cuda.synchronize()
+    finally:
+        spffn.set_wait_limit(spffn.WAIT_LIMIT_DEFAULT)
+    assert torch.isnan(h).all()
+    again = spffn.decode_step(model, x)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref)  # bitwise: fixed summation order
+
+
 def _model(cfg, tau, layers=2):
     ws = [make_layer(replace(cfg, tau=tau), l, seed=7, n_cal=512) for l in range(layers)]
     return spffn.Model([gpu_layer(w) for w in ws], rms_eps=1e-5)
