@@ -966,14 +966,17 @@ int fused_groups(const Layer &L) {
 }
 
 // Down-projection chunks: ranges of NG consecutive row groups, NG <= 64 (so a
-// chunk's slots fit the down workgroup's LDS list), at least 128 chunks when
-// there are that many groups (smaller chunks complete sooner after their last
-// group; measured at the 70B shape: 32 chunks 4.15 ms per step, 64 3.87,
-// 96 3.86, 128 3.83-3.84, 192 4.00, 256 4.27).
+// chunk's slots fit the down workgroup's LDS list), at least 128 chunks (192
+// for 4-bit rows) when there are that many groups: smaller chunks complete
+// sooner after their last group, more of them cost more partial sums.
+// Measured per step, 70B shape: 32 chunks 4.15 ms, 64 3.87, 96 3.86, 128
+// 3.83, 192 4.00, 256 4.27; 7B: 64 0.810, 128 0.802, 192 0.827; 175B 4-bit:
+// 64 8.21, 128 7.46, 192 7.32, 256 7.33.
 int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
+    const int cmin = L.desc.w_dtype == SPFFN_Q4_0 ? 192 : 128;
     int c = (G + 63) / 64;
-    if (c < 128) c = 128;
+    if (c < cmin) c = cmin;
     if (c > G) c = G;
     return (G + c - 1) / c;
 }
