@@ -3,14 +3,20 @@ computes: every replay (with other eager work and synchronisation between
 replays, and a new input written into the captured x each time) is compared
 bit for bit with an eager decode_step on the same input, which the other GPU
 tests check against the oracle."""
+from dataclasses import replace
+
 import pytest
 import torch
 
 import activation_sparse_mlp_amd as spffn
-from tests.gpu_helpers import DEV
-from workloads import LLAMA2_7B, TINY, make_layer, make_tokens
+from tests.gpu_helpers import DEV, gpu_layer
+from tests.test_gpu_mixed import CFGS as MIXED
+from workloads import LLAMA2_7B, OPT_175B_Q4, TINY, make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
+
+# 4-bit rows at a small shape; 1530 neurons leave the last 20-row group ragged
+_Q4 = replace(OPT_175B_Q4, d=512, d_ffn=1530, r=64)
 
 
 def setup_module(module):
@@ -19,7 +25,9 @@ def setup_module(module):
 
 
 def _model(cfg, layers):
-    gl = [spffn.Layer(make_layer(cfg, l, seed=0, device=DEV, n_cal=512)) for l in range(layers)]
+    # 4-bit layers are generated on the host, as in the parity tests
+    dev = "cpu" if cfg.w_dtype == "q4_0" else DEV
+    gl = [gpu_layer(make_layer(cfg, l, seed=0, device=dev, n_cal=512)) for l in range(layers)]
     return spffn.Model(gl, rms_eps=1e-5)
 
 
@@ -29,13 +37,27 @@ def _model(cfg, layers):
     (LLAMA2_7B, 2, 4, False),     # batched union path
     (LLAMA2_7B, 1, 12, False),    # batched, two row tiles per workgroup
     (LLAMA2_7B, 1, 1, True),      # dense baseline
+    (_Q4, 2, 1, False),           # 4-bit rows, single-token fused path
+    (_Q4, 2, 3, False),           # 4-bit rows, batched vector path
 ])
 def test_graph_replays_match_eager(cfg, layers, B, dense):
     print(f"graph {cfg.name} layers={layers} B={B} dense={dense}", flush=True)
-    model = _model(cfg, layers)
-    xs = make_tokens(cfg.d, 4, B, seed=9, device=DEV)
-    xbuf = torch.empty(B, cfg.d, device=DEV)
-    hbuf = torch.empty(B, cfg.d, device=DEV)
+    _replays_match_eager(_model(cfg, layers), cfg.d, layers, B, dense, cfg.d_ffn)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_graph_mixed_stack(B):
+    """Layers of different kinds, formats and shapes (per-kernel path at one
+    token; matrix-core and vector layers in turn at three)."""
+    print(f"graph mixed stack B={B}", flush=True)
+    gl = [gpu_layer(make_layer(c, l, seed=3, n_cal=512)) for l, c in enumerate(MIXED)]
+    _replays_match_eager(spffn.Model(gl, rms_eps=1e-5), MIXED[0].d, len(MIXED), B, False, None)
+
+
+def _replays_match_eager(model, d, layers, B, dense, d_ffn):
+    xs = make_tokens(d, 4, B, seed=9, device=DEV)
+    xbuf = torch.empty(B, d, device=DEV)
+    hbuf = torch.empty(B, d, device=DEV)
     cnt = torch.full((layers,), -1, dtype=torch.int32, device=DEV)
     g = spffn.DecodeGraph(model, xbuf, hbuf, dense=dense, layer_counts=cnt)
     torch.cuda.synchronize()
@@ -55,7 +77,7 @@ def test_graph_replays_match_eager(cfg, layers, B, dense):
         assert torch.equal(got_h, ref_h), f"replay {rep}: h differs"
         assert torch.equal(got_c, ref_c), f"replay {rep}: layer counts differ"
         if dense:
-            assert all(int(c) == cfg.d_ffn for c in got_c)
+            assert all(int(c) == d_ffn for c in got_c)
     del g
 
 
