@@ -384,6 +384,36 @@ def test_decode_layer_batch_union():
         assert np.array_equal(out["y"][b], oracle.ffn_masked(L, n, out["union"]))
 
 
+def _one_neuron_layer(v):
+    """d = 4, two ReLU neurons, predictor fixed to fire neuron 0 only (zero
+    weights, logit biases +5 / -5); neuron 0 reads n[0] and writes v, neuron 1
+    would add 1000 everywhere if it were ever computed."""
+    f = lambda a: np.asarray(a, dtype=np.float32)  # noqa: E731
+    return dict(kind="relu", w_dtype="f32", p_dtype="f32", d=4, d_ffn=2, r=1, w_gate=None,
+                w_up=f([[1, 0, 0, 0], [1, 1, 1, 1]]), w_down_t=f([v, [1000] * 4]),
+                b_act=f([0, 0]), p_w1=f([[0, 0, 0, 0]]), p_b1=f([0]), p_w2=f([[0], [0]]),
+                p_b2=f([5, -5]), t=0.0)
+
+
+def test_decode_step_two_layers_closed_form():
+    """A constant vector h = a stays constant through these layers: each adds
+    b * max(s(h), 0), s(z) = z / sqrt(z^2 + eps) being the RMS-normalised
+    entry (all neurons but the first predicted off).  The order of the layers,
+    the residual, the ReLU and the carried state all show in the result."""
+    eps, a, b1, b2 = 0.5, 1.5, 0.25, -2.0
+    A, B = _one_neuron_layer([b1] * 4), _one_neuron_layer([b2] * 4)
+    step = lambda z, b: z + b * max(z / math.sqrt(z * z + eps), 0.0)  # noqa: E731
+    want_ab = step(step(a, b1), b2)
+    got = oracle.decode_step([A, B], np.full((1, 4), a), eps)
+    np.testing.assert_allclose(got, np.full((1, 4), want_ab), rtol=1e-14)
+    # the other order: B drives h negative, so A's neuron stays off
+    want_ba = step(step(a, b2), b1)
+    assert step(a, b2) < 0 and want_ba == step(a, b2)
+    got_ba = oracle.decode_step([B, A], np.full((1, 4), a), eps)
+    np.testing.assert_allclose(got_ba, np.full((1, 4), want_ba), rtol=1e-14)
+    assert abs(want_ab - want_ba) > 1e-3
+
+
 # --------------------------------------------------------------------------- #
 # profile and hot-first permutation
 # --------------------------------------------------------------------------- #
