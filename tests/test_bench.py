@@ -48,6 +48,9 @@ def test_dominant_kernel_bytes_by_hand():
     # ReLU: up + down rows of 8 fp32 values
     assert bench.dominant_kernel_bytes(_layer(kind="relu", w_dtype="f32"), 2, 1) == \
         32 * 13 + 2 * (2 * 32 + 4 + 8) + (4 + 8) * 4
+    # ReLU with 4-bit rows, d = 64: two 18-byte blocks per row
+    assert bench.dominant_kernel_bytes(_layer(kind="relu", w_dtype="q4_0", d=64), 3, 1) == \
+        32 * 13 + 3 * (2 * 36 + 4 + 8) + (4 + 64) * 4
 
 
 def test_batched_ffn_bytes_by_hand():
