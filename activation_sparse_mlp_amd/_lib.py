@@ -53,6 +53,8 @@ SIGNATURES = {
     "spffn_model_destroy": (None, [_vp]),
     "spffn_layer_workspace_bytes": (_sz, [_vp, _i32]),
     "spffn_model_workspace_bytes": (_sz, [_vp, _i32]),
+    "spffn_workspace_clear_status": (_i32, [_vp, _sz, _vp]),
+    "spffn_workspace_status": (_i32, [_vp, _sz, _vp, _vp]),
     "spffn_threshold": (_i32, [_vp, _i64, _f32, _vp, _vp]),
     "spffn_compact": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "spffn_predict": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -67,6 +69,7 @@ SIGNATURES = {
     "spffn_hot_first_order": (_i32, [_vp, _i32, _vp, _vp]),
     "spffn_permute_rows": (_i32, [_vp, _vp, _vp, _i32, _i64, _vp]),
     "spffn_q4_0_repack": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "spffn_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
     "spffn_set_wait_limit": (_i32, [_i32]),
     "spffn_last_error": (C.c_char_p, []),
     "spffn_version": (C.c_char_p, []),
@@ -105,16 +108,53 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, n=None, at_least=False):
+    """Check a tensor argument: its size first (n elements, or at least n), so
+    that a wrongly sized buffer is rejected whatever its device, then that it
+    is a contiguous HIP tensor of the given dtype."""
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if n is not None:
+        _size(t, n, name, at_least)
+    if not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _size(t, n, name, at_least=False):
+    """Raise ValueError unless tensor t holds exactly n elements (at least n
+    with at_least).  The C entry points receive bare pointers, so every length
+    is checked here, before anything is enqueued."""
+    if t is None:
+        return
+    k = t.numel()
+    if (k < n) if at_least else (k != n):
+        want = f">= {n}" if at_least else f"{n}"
+        raise ValueError(f"{name} holds {k} elements, needs {want}")
+
+
+def _tokens(x, d, name="x"):
+    """Number of tokens B of an activation tensor x of shape [d] or [B, d]."""
+    if x.dim() not in (1, 2) or x.shape[-1] != d:
+        raise ValueError(f"{name} must have shape [d] or [B, d] with d={d}, got "
+                         f"{tuple(x.shape)}")
+    return x.shape[0] if x.dim() == 2 else 1
+
+
+def _ws_bytes(ws, need, name="ws"):
+    """Byte size of a caller workspace tensor (any dtype), checked against need."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA (HIP) tensor")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"{name} has {nbytes} bytes, needs {need}")
+    return nbytes
 
 
 def version():
@@ -147,17 +187,30 @@ class Layer:
         self.tau = float(w["tau"])
         wd = {"f32": torch.float32, "f16": torch.float16, "q4_0": torch.uint8}[self.w_dtype]
         pd = {"f32": torch.float32, "f16": torch.float16}[self.p_dtype]
+        if min(self.d, self.d_ffn, self.r) <= 0:
+            raise ValueError(f"d={self.d}, d_ffn={self.d_ffn}, r={self.r} must be positive")
+        if self.w_dtype == "q4_0" and self.d % 32:
+            raise ValueError(f"4-bit rows need d % 32 == 0, got d={self.d}")
+        n_w = self.d_ffn * (self.d // 32 * 18 if self.w_dtype == "q4_0" else self.d)
+        sizes = {"w_gate": n_w, "w_up": n_w, "w_down_t": n_w, "b_act": self.d_ffn,
+                 "p_w1": self.r * self.d, "p_b1": self.r, "p_w2": self.d_ffn * self.r,
+                 "p_b2": self.d_ffn}
+        for k, n in sizes.items():  # every size before any device check
+            if isinstance(w.get(k), torch.Tensor) and (k != "w_gate" or self.kind == "reglu"):
+                _size(w[k], n, k)
         t = {}
         for k in ("w_gate", "w_up", "w_down_t"):
             if w.get(k) is not None and (k != "w_gate" or self.kind == "reglu"):
-                t[k] = _dev(w[k], wd, k)
+                t[k] = _dev(w[k], wd, k, n_w)
                 if self.w_dtype == "q4_0":
                     t[k] = q4_0_repack(t[k], self.d_ffn, self.d)
-        t["b_act"] = _dev(w.get("b_act"), torch.float32, "b_act")
-        for k in ("p_w1", "p_w2"):
-            t[k] = _dev(w[k], pd, k)
-        for k in ("p_b1", "p_b2"):
-            t[k] = _dev(w[k], torch.float32, k)
+        if "w_up" not in t or "w_down_t" not in t or (self.kind == "reglu" and "w_gate" not in t):
+            raise ValueError("missing FFN weight (w_up, w_down_t, and w_gate for ReGLU)")
+        t["b_act"] = _dev(w.get("b_act"), torch.float32, "b_act", self.d_ffn)
+        for k, n in (("p_w1", self.r * self.d), ("p_w2", self.d_ffn * self.r)):
+            t[k] = _dev(w[k], pd, k, n)
+        for k, n in (("p_b1", self.r), ("p_b2", self.d_ffn)):
+            t[k] = _dev(w[k], torch.float32, k, n)
         self.tensors = t
         desc = LayerDesc(d=self.d, d_ffn=self.d_ffn, r=self.r, kind=_KINDS[self.kind],
                          w_dtype=_DTYPES[self.w_dtype], p_dtype=_DTYPES[self.p_dtype],
@@ -175,10 +228,13 @@ class Layer:
         return int(load().spffn_layer_workspace_bytes(self.handle, B))
 
     def workspace(self, B, device=None):
+        """A workspace for B tokens, its status word cleared."""
         n = self.workspace_bytes(B)
         if n == 0:
             raise SpffnError(-2, "workspace_bytes", f"bad batch {B}")
-        return torch.empty(n, dtype=torch.uint8, device=device or self.tensors["w_up"].device)
+        ws = torch.empty(n, dtype=torch.uint8, device=device or self.tensors["w_up"].device)
+        workspace_clear_status(ws)
+        return ws
 
     def __del__(self):
         if getattr(self, "handle", None) is not None and _lib is not None:
@@ -199,15 +255,20 @@ class Model:
         self.handle = h
         self.rms_eps = rms_eps
         self.d = self.layers[0].d
+        self.n_layers = len(self.layers)
+        self.sum_d_ffn = sum(l.d_ffn for l in self.layers)
 
     def workspace_bytes(self, B):
         return int(load().spffn_model_workspace_bytes(self.handle, B))
 
     def workspace(self, B):
+        """A workspace for B tokens, its status word cleared."""
         n = self.workspace_bytes(B)
         if n == 0:
             raise SpffnError(-2, "model_workspace_bytes", f"bad batch {B}")
-        return torch.empty(n, dtype=torch.uint8, device=self.layers[0].tensors["w_up"].device)
+        ws = torch.empty(n, dtype=torch.uint8, device=self.layers[0].tensors["w_up"].device)
+        workspace_clear_status(ws)
+        return ws
 
     def __del__(self):
         if getattr(self, "handle", None) is not None and _lib is not None:
@@ -218,11 +279,32 @@ class Model:
 # --------------------------------------------------------------------------- #
 # entry points (same names as the C ABI, without the prefix)
 # --------------------------------------------------------------------------- #
+def workspace_clear_status(ws):
+    """Zero the status block at the start of a workspace (on the current stream)."""
+    nb = _ws_bytes(ws, 256)
+    _check(load().spffn_workspace_clear_status(_ptr(ws), nb, _stream()),
+           "spffn_workspace_clear_status")
+
+
+def workspace_status(ws, out=None):
+    """Device int32 [1]: the number of bounded in-launch waits that gave up
+    since the workspace's status was last cleared (0 on a healthy run)."""
+    nb = _ws_bytes(ws, 256)
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=ws.device)
+    _dev(out, torch.int32, "out", 1, at_least=True)
+    _check(load().spffn_workspace_status(_ptr(ws), nb, _ptr(out), _stream()),
+           "spffn_workspace_status")
+    return out
+
+
 def threshold(logits, t, mask=None):
+    if mask is not None:
+        _size(mask, logits.numel(), "mask")
     logits = _dev(logits, torch.float32, "logits")
     if mask is None:
         mask = torch.empty(logits.shape, dtype=torch.uint8, device=logits.device)
-    _dev(mask, torch.uint8, "mask")
+    _dev(mask, torch.uint8, "mask", logits.numel())
     _check(load().spffn_threshold(_ptr(logits), logits.numel(), float(t), _ptr(mask), _stream()),
            "spffn_threshold")
     return mask
@@ -230,16 +312,18 @@ def threshold(logits, t, mask=None):
 
 def compact(mask, idx=None, count=None):
     """(idx int32 [n], count int32 [1]) on the device; idx[:count] is valid."""
+    n = mask.numel()
+    _size(idx, n, "idx", at_least=True)
+    _size(count, 1, "count", at_least=True)
     mask = _dev(mask, None, "mask")
     if mask.dtype not in (torch.uint8, torch.bool):
         raise TypeError("mask must be uint8 or bool")
-    n = mask.numel()
     if idx is None:
         idx = torch.empty(n, dtype=torch.int32, device=mask.device)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=mask.device)
-    _dev(idx, torch.int32, "idx")
-    _dev(count, torch.int32, "count")
+    _dev(idx, torch.int32, "idx", n, at_least=True)
+    _dev(count, torch.int32, "count", 1, at_least=True)
     _check(load().spffn_compact(_ptr(mask), n, _ptr(idx), _ptr(count), _stream()),
            "spffn_compact")
     return idx, count
@@ -256,15 +340,22 @@ def _opt(v, shape, dtype, dev):
 def predict(layer, x, logits=True, mask=True, union=True, ws=None):
     """Returns dict(logits [B, d_ffn] f32, mask [B, d_ffn] u8, union [d_ffn] u8);
     pass False for an output that is not wanted, or a tensor to write into."""
+    B = _tokens(x, layer.d)
+    for v, n, name in ((logits, B * layer.d_ffn, "logits"), (mask, B * layer.d_ffn, "mask"),
+                       (union, layer.d_ffn, "union")):
+        if isinstance(v, torch.Tensor):
+            _size(v, n, name)
     x = _dev(x, torch.float32, "x")
-    B = x.shape[0] if x.dim() == 2 else 1
     dev = x.device
-    lg = _dev(_opt(logits, (B, layer.d_ffn), torch.float32, dev), torch.float32, "logits")
-    mk = _dev(_opt(mask, (B, layer.d_ffn), torch.uint8, dev), torch.uint8, "mask")
-    un = _dev(_opt(union, (layer.d_ffn,), torch.uint8, dev), torch.uint8, "union")
+    lg = _dev(_opt(logits, (B, layer.d_ffn), torch.float32, dev), torch.float32, "logits",
+              B * layer.d_ffn)
+    mk = _dev(_opt(mask, (B, layer.d_ffn), torch.uint8, dev), torch.uint8, "mask",
+              B * layer.d_ffn)
+    un = _dev(_opt(union, (layer.d_ffn,), torch.uint8, dev), torch.uint8, "union", layer.d_ffn)
     ws = layer.workspace(B) if ws is None else ws
+    nb = _ws_bytes(ws, layer.workspace_bytes(B))
     _check(load().spffn_predict(layer.handle, _ptr(x), B, _ptr(lg), _ptr(mk), _ptr(un), _ptr(ws),
-                                ws.numel(), _stream()), "spffn_predict")
+                                nb, _stream()), "spffn_predict")
     out = {}
     for k, v in (("logits", lg), ("mask", mk), ("union", un)):
         if v is not None:
@@ -273,20 +364,30 @@ def predict(layer, x, logits=True, mask=True, union=True, ws=None):
 
 
 def forward(layer, x, mask=None, idx=None, count=None, y=None, ws=None):
-    """y [B, d] of the FFN over the given neuron set (dense if none is given)."""
+    """y [B, d] of the FFN over the given neuron set (dense if none is given).
+
+    idx must have room for d_ffn entries: the count lives on the device, so a
+    shorter list could not be checked against it without a synchronisation."""
+    B = _tokens(x, layer.d)
+    if mask is None and (idx is None) != (count is None):
+        raise ValueError("idx and count must be given together")
+    _size(y, B * layer.d, "y")
+    _size(mask, layer.d_ffn, "mask")
+    _size(idx, layer.d_ffn, "idx", at_least=True)
+    _size(count, 1, "count", at_least=True)
     x = _dev(x, torch.float32, "x")
-    B = x.shape[0] if x.dim() == 2 else 1
     if y is None:
         y = torch.empty_like(x)
-    _dev(y, torch.float32, "y")
+    _dev(y, torch.float32, "y", B * layer.d)
     if mask is not None and mask.dtype not in (torch.uint8, torch.bool):
         raise TypeError("mask must be uint8 or bool")
-    _dev(mask, None, "mask")
-    _dev(idx, torch.int32, "idx")
-    _dev(count, torch.int32, "count")
+    _dev(mask, None, "mask", layer.d_ffn)
+    _dev(idx, torch.int32, "idx", layer.d_ffn, at_least=True)
+    _dev(count, torch.int32, "count", 1, at_least=True)
     ws = layer.workspace(B) if ws is None else ws
+    nb = _ws_bytes(ws, layer.workspace_bytes(B))
     _check(load().spffn_forward(layer.handle, _ptr(x), B, _ptr(mask), _ptr(idx), _ptr(count),
-                                _ptr(y), _ptr(ws), ws.numel(), _stream()), "spffn_forward")
+                                _ptr(y), _ptr(ws), nb, _stream()), "spffn_forward")
     return y
 
 
@@ -295,22 +396,35 @@ def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws
     dict with device tensors h_in [L, B, d] f32, union_mask [sum d_ffn] u8,
     logits [sum B*d_ffn] f32, and `events`, a ctypes array of 2L hipEvent_t
     handles recorded around each layer's largest kernel."""
-    x = _dev(x, torch.float32, "x")
-    B = x.shape[0] if x.dim() == 2 else 1
-    if h is None:
-        h = torch.empty_like(x)
-    _dev(h, torch.float32, "h")
-    _dev(layer_counts, torch.int32, "layer_counts")
+    B = _tokens(x, model.d)
+    _size(h, B * model.d, "h")
+    _size(layer_counts, model.n_layers, "layer_counts", at_least=True)
     tr = None
     if trace is not None:
         ev = trace.get("events")
-        tr = Trace(h_in=_ptr(trace.get("h_in")), union_mask=_ptr(trace.get("union_mask")),
-                   logits=_ptr(trace.get("logits")),
+        sizes = {"h_in": model.n_layers * B * model.d, "union_mask": model.sum_d_ffn,
+                 "logits": B * model.sum_d_ffn}
+        for k, n in sizes.items():
+            _size(trace.get(k), n, f"trace {k}", at_least=True)
+        if ev is not None and len(ev) < 2 * model.n_layers:
+            raise ValueError(f"trace events holds {len(ev)} handles, needs "
+                             f">= {2 * model.n_layers}")
+    x = _dev(x, torch.float32, "x")
+    if h is None:
+        h = torch.empty_like(x)
+    _dev(h, torch.float32, "h", B * model.d)
+    _dev(layer_counts, torch.int32, "layer_counts", model.n_layers, at_least=True)
+    if trace is not None:
+        h_in = _dev(trace.get("h_in"), torch.float32, "trace h_in")
+        um = _dev(trace.get("union_mask"), torch.uint8, "trace union_mask")
+        lg = _dev(trace.get("logits"), torch.float32, "trace logits")
+        tr = Trace(h_in=_ptr(h_in), union_mask=_ptr(um), logits=_ptr(lg),
                    events=None if ev is None else C.cast(ev, C.c_void_p))
     ws = model.workspace(B) if ws is None else ws
+    nb = _ws_bytes(ws, model.workspace_bytes(B))
     _check(load().spffn_decode_step(model.handle, _ptr(x), _ptr(h), B,
                                     DECODE_DENSE if dense else 0, _ptr(layer_counts),
-                                    C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),
+                                    C.byref(tr) if tr is not None else None, _ptr(ws), nb,
                                     _stream()), "spffn_decode_step")
     return h
 
@@ -323,18 +437,21 @@ class DecodeGraph:
     `x` and call launch() once per token."""
 
     def __init__(self, model, x, h=None, dense=False, layer_counts=None, ws=None):
+        B = _tokens(x, model.d)
+        _size(h, B * model.d, "h")
+        _size(layer_counts, model.n_layers, "layer_counts", at_least=True)
         x = _dev(x, torch.float32, "x")
-        B = x.shape[0] if x.dim() == 2 else 1
         if h is None:
             h = torch.empty_like(x)
-        _dev(h, torch.float32, "h")
-        _dev(layer_counts, torch.int32, "layer_counts")
+        _dev(h, torch.float32, "h", B * model.d)
+        _dev(layer_counts, torch.int32, "layer_counts", model.n_layers, at_least=True)
         ws = model.workspace(B) if ws is None else ws
+        nb = _ws_bytes(ws, model.workspace_bytes(B))
         self.model, self.x, self.h, self.layer_counts, self.ws = model, x, h, layer_counts, ws
         out = _vp()
         _check(load().spffn_decode_graph_create(model.handle, _ptr(x), _ptr(h), B,
                                                 DECODE_DENSE if dense else 0, _ptr(layer_counts),
-                                                _ptr(ws), ws.numel(), C.byref(out)),
+                                                _ptr(ws), nb, C.byref(out)),
                "spffn_decode_graph_create")
         self.handle = out.value
 
@@ -351,21 +468,23 @@ class DecodeGraph:
 
 def profile(layer, x, counts=None):
     """counts int32 [d_ffn] += tokens of x [N, d] with a positive pre-activation."""
+    N = _tokens(x, layer.d)
+    _size(counts, layer.d_ffn, "counts")
     x = _dev(x, torch.float32, "x")
-    N = x.shape[0] if x.dim() == 2 else 1
     if counts is None:
         counts = torch.zeros(layer.d_ffn, dtype=torch.int32, device=x.device)
-    _dev(counts, torch.int32, "counts")
+    _dev(counts, torch.int32, "counts", layer.d_ffn)
     _check(load().spffn_profile(layer.handle, _ptr(x), N, _ptr(counts), None, 0, _stream()),
            "spffn_profile")
     return counts
 
 
 def hot_first_order(counts, perm=None):
+    _size(perm, counts.numel(), "perm")
     counts = _dev(counts, torch.int32, "counts")
     if perm is None:
         perm = torch.empty_like(counts)
-    _dev(perm, torch.int32, "perm")
+    _dev(perm, torch.int32, "perm", counts.numel())
     _check(load().spffn_hot_first_order(_ptr(counts), counts.numel(), _ptr(perm), _stream()),
            "spffn_hot_first_order")
     return perm
@@ -373,12 +492,16 @@ def hot_first_order(counts, perm=None):
 
 def permute_rows(src, perm, dst=None):
     """dst[k] = src[perm[k]] along dim 0 (any dtype, rows of a multiple of 4 bytes)."""
+    if src.dim() < 1 or src.shape[0] < 1:
+        raise ValueError("src must have at least one row")
+    rows = src.shape[0]
+    _size(perm, rows, "perm")
+    _size(dst, src.numel(), "dst")
     src = _dev(src, None, "src")
-    _dev(perm, torch.int32, "perm")
+    _dev(perm, torch.int32, "perm", rows)
     if dst is None:
         dst = torch.empty_like(src)
-    _dev(dst, src.dtype, "dst")
-    rows = src.shape[0]
+    _dev(dst, src.dtype, "dst", src.numel())
     row_bytes = src.numel() * src.element_size() // rows
     _check(load().spffn_permute_rows(_ptr(src), _ptr(dst), _ptr(perm), rows, row_bytes,
                                      _stream()), "spffn_permute_rows")
@@ -386,13 +509,30 @@ def permute_rows(src, perm, dst=None):
 
 
 def q4_0_repack(aos, rows, cols, soa=None):
-    aos = _dev(aos, torch.uint8, "aos")
+    if rows < 1 or cols < 32 or cols % 32:
+        raise ValueError(f"rows={rows}, cols={cols}: need rows >= 1 and cols a multiple of 32")
+    n = rows * (cols // 32) * 18
+    _size(soa, n, "soa")
+    aos = _dev(aos, torch.uint8, "aos", n)
     if soa is None:
-        soa = torch.empty(rows * (cols // 32) * 18, dtype=torch.uint8, device=aos.device)
-    _dev(soa, torch.uint8, "soa")
+        soa = torch.empty(n, dtype=torch.uint8, device=aos.device)
+    _dev(soa, torch.uint8, "soa", n)
     _check(load().spffn_q4_0_repack(_ptr(aos), _ptr(soa), rows, cols, _stream()),
            "spffn_q4_0_repack")
     return soa
+
+
+def stream_read(buf, sink=None):
+    """Read every byte of a device tensor once (bandwidth probe); returns the
+    device uint32 sink the data is folded into."""
+    buf = _dev(buf, None, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _dev(sink, torch.int32, "sink", 1, at_least=True)
+    _check(load().spffn_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()),
+           "spffn_stream_read")
+    return sink
 
 
 # rows that move together under a neuron permutation

@@ -65,6 +65,7 @@ WMat wmat(const void *p, int dtype, int rows, int cols) {
 }
 
 struct Ws {
+    int32_t *status;
     float *n, *hid, *act, *part, *scale, *lst_a, *w1p;
     uint8_t *mask, *uni;
     int32_t *idx, *count, *gcnt, *lst_i, *done;
@@ -79,6 +80,7 @@ Ws carve(const Layer &L, int B, void *ws) {
     WsLayout lo = layer_ws_layout(L, B);
     uint8_t *base = static_cast<uint8_t *>(ws);
     Ws w;
+    w.status = reinterpret_cast<int32_t *>(base + lo.status);
     w.n = reinterpret_cast<float *>(base + lo.n);
     w.hid = reinterpret_cast<float *>(base + lo.hid);
     w.mask = base + lo.mask;
@@ -224,7 +226,8 @@ WsLayout layer_ws_layout(const Layer &L, int B) {
     const spffn_layer_desc &D = L.desc;
     WsLayout lo{};
     lo.chunks = down_chunks(L);
-    size_t off = 0;
+    lo.status = 0;
+    size_t off = kWsStatusBytes;
     // The batched decode hands these from layer to layer, so they come first:
     // their offsets depend only on B and d, the same for every layer.
     const bool mf = B > 1 && mfma_fits(L, B);
@@ -331,7 +334,7 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
         const int chunks = fused_chunks(L);
         int32_t *lc = layer_counts ? layer_counts + l : nullptr;
         SPFFN_HIP(launch_layer_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, w.done, w.part,
-                                  lc ? w.gcnt : nullptr, s, e0, e1),
+                                  lc ? w.gcnt : nullptr, w.status, s, e0, e1),
                   "predictor layer-2 + gather + down launch");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
@@ -473,6 +476,30 @@ size_t spffn_model_workspace_bytes(const spffn_model *model, int32_t B) {
         if (v > m) m = v;
     }
     return m;
+}
+
+spffn_status spffn_workspace_clear_status(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return fail(SPFFN_E_ARG, "workspace_clear_status: NULL workspace");
+    if (!aligned(ws, 256)) return fail(SPFFN_E_ARG, "workspace must be 256-byte aligned");
+    if (ws_bytes < kWsStatusBytes)
+        return fail(SPFFN_E_WORKSPACE, "workspace has %zu bytes, less than its status block",
+                    ws_bytes);
+    SPFFN_HIP(launch_fill_i32(static_cast<int32_t *>(ws), 0, (int)(kWsStatusBytes / 4),
+                              (hipStream_t)stream),
+              "status clear launch");
+    return SPFFN_OK;
+}
+
+spffn_status spffn_workspace_status(const void *ws, size_t ws_bytes, int32_t *giveups,
+                                    void *stream) {
+    if (!ws || !giveups) return fail(SPFFN_E_ARG, "workspace_status: NULL pointer");
+    if (!aligned(ws, 256) || !aligned(giveups, 4))
+        return fail(SPFFN_E_ARG, "workspace_status: misaligned workspace or output");
+    if (ws_bytes < kWsStatusBytes)
+        return fail(SPFFN_E_WORKSPACE, "workspace has %zu bytes, less than its status block",
+                    ws_bytes);
+    SPFFN_HIP(launch_copy_words(ws, giveups, 1, (hipStream_t)stream), "status copy launch");
+    return SPFFN_OK;
 }
 
 spffn_status spffn_threshold(const float *logits, int64_t n, float t, uint8_t *mask,
@@ -734,6 +761,17 @@ spffn_status spffn_permute_rows(const void *src, void *dst, const int32_t *perm,
         return fail(SPFFN_E_ARG, "permute_rows: src and dst overlap");
     SPFFN_HIP(launch_permute_rows(src, dst, perm, rows, row_bytes, (hipStream_t)stream),
               "permute_rows launch");
+    return SPFFN_OK;
+}
+
+spffn_status spffn_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return fail(SPFFN_E_ARG, "stream_read: NULL pointer");
+    if (bytes < 16 || bytes % 16)
+        return fail(SPFFN_E_SHAPE, "stream_read: bytes=%lld must be a positive multiple of 16",
+                    (long long)bytes);
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return fail(SPFFN_E_ARG, "stream_read: buf must be 16-byte, sink 4-byte aligned");
+    SPFFN_HIP(launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream_read launch");
     return SPFFN_OK;
 }
 

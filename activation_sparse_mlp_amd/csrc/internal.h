@@ -32,6 +32,7 @@ struct Layer {
 
 // Workspace carve-up for a batch of B tokens.
 struct WsLayout {
+    size_t status;  // kWsStatusBytes at offset 0: int32 count of bounded waits that gave up
     size_t n, hid, mask, uni, idx, count, scale, act, gcnt, lst_i, lst_a, done, part, total;
     size_t xhi, xlo, hhi, hlo, ahi, alo, w1p;  // fp16 splits and partials of the batched path
     size_t tmask;                              // union bits per 16-row tile (batched path)
@@ -39,6 +40,10 @@ struct WsLayout {
     int ld_act;  // row pitch (elements) of ahi / alo
     int chunks;  // neuron chunks of the down projection (partial-sum slots)
 };
+
+// Every workspace starts with a status block; its first int32 counts the
+// down-projection workgroups whose bounded in-launch wait gave up.
+constexpr size_t kWsStatusBytes = 256;
 
 WsLayout layer_ws_layout(const Layer &L, int B);
 
@@ -75,6 +80,8 @@ hipError_t launch_reduce(const float *part, int chunks, int B, int d, const floa
 hipError_t launch_rmsnorm(const float *h, int B, int d, float eps, float *n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, int n, hipStream_t s);
 hipError_t launch_copy_words(const void *src, void *dst, int64_t n_words, hipStream_t s);
+// measurement: read bytes (a multiple of 16) of buf once, folding into *sink
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
 
 int down_chunks(const Layer &L);
 hipError_t launch_rms_scale(const float *h, int B, int d, float eps, float *scale, hipStream_t s);
@@ -143,9 +150,12 @@ constexpr int kFusedDoneStride = 1024;
 constexpr int kChunkWaitPollsDefault = 1 << 18;
 constexpr int kChunkWaitPollsMax = 1 << 24;
 void set_chunk_wait_polls(int polls);
+// giveups: device int32, incremented once per down-projection workgroup whose
+// wait runs out (it then writes NaN partial sums and lists no rows).
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
-                           int32_t *done, float *part, int32_t *chunk_cnt, hipStream_t s,
-                           hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                           int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
+                           hipStream_t s, hipEvent_t ev_start = nullptr,
+                           hipEvent_t ev_stop = nullptr);
 
 }  // namespace spffn

@@ -651,6 +651,7 @@ struct DownListArgs {
     float *part;           // [chunks, d]
     int32_t *chunk_cnt;    // [chunks] rows listed per chunk, or nullptr
     int wait_polls;        // polls before giving up on a chunk
+    int32_t *giveups;      // device count of workgroups that gave up waiting
 };
 
 constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 64, rows per group <= 20
@@ -674,9 +675,14 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
     const size_t base = (size_t)g0 * a.RB;
     const int col0 = slice * 64 * E;
     if (!ready) {
-        // the chunk's lists never arrived: poison the partial sums
+        // the chunk's lists never arrived: poison the partial sums, list no
+        // rows, and count the give-up in the workspace status word
         for (int t = threadIdx.x; t < 64 * E; t += blockDim.x)
             if (col0 + t < a.d) a.part[(size_t)c * a.d + col0 + t] = __builtin_nanf("");
+        if (threadIdx.x == 0) {
+            if (a.chunk_cnt && slice == 0) a.chunk_cnt[c] = 0;
+            __hip_atomic_fetch_add(a.giveups, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         return;
     }
 
@@ -1039,8 +1045,8 @@ static void launch_layer_kind(const FusedArgs &f, const DownListArgs &dn, bool g
 
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
-                           int32_t *done, float *part, int32_t *chunk_cnt, hipStream_t s,
-                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+                           int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
+                           hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
     const bool gated = D.kind == SPFFN_REGLU;
     const int G = fused_groups(L), UA = fused_ua(L), C = fused_chunks(L), NG = fused_per_chunk(L);
@@ -1078,6 +1084,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     dn.part = part;
     dn.chunk_cnt = chunk_cnt;
     dn.wait_polls = g_chunk_wait_polls.load();
+    dn.giveups = giveups;
     const int blocks = G + C * slices;
     if (D.p_dtype == SPFFN_F16) {
         if (D.w_dtype == SPFFN_F16)

@@ -278,6 +278,49 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
     for (int k = threadIdx.x; k < d; k += blockDim.x) ob[k] = hb[k] / den;
 }
 
+// ---------------------------------------------------------------------------
+// stream read (measurement only): every 16-byte word of a buffer is read once
+// with a non-temporal load, 8 loads in flight per thread; each workgroup folds
+// its words with XOR and XORs the result into *sink, so no load can be
+// dropped.  Its bandwidth is the read ceiling the decode kernels are compared
+// with.
+// ---------------------------------------------------------------------------
+typedef unsigned int stream_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p,
+                                                          int64_t n16, uint32_t *sink) {
+    constexpr int U = 8;
+    __shared__ uint32_t red[4];
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += stride) {
+        stream_u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            v[u] = i < n16 ? __builtin_nontemporal_load(
+                                 reinterpret_cast<const stream_u32x4 *>(p + i))
+                           : stream_u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicXor(sink, red[0] ^ red[1] ^ red[2] ^ red[3]);
+}
+
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    int64_t blocks = (n16 + 256 * 8 - 1) / (256 * 8);
+    if (blocks > 2048) blocks = 2048;  // eight workgroups per CU, grid-stride beyond that
+    if (blocks < 1) blocks = 1;
+    stream_read_kernel<<<(int)blocks, 256, 0, s>>>(static_cast<const uint4 *>(buf), n16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const float *h, int B, int d, float eps, float *n, hipStream_t s) {
     rmsnorm_kernel<<<B, 256, 0, s>>>(h, d, eps, n);
     return hipGetLastError();

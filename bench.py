@@ -45,7 +45,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="use only the first N layers (experiments; not the headline config)")
     ap.add_argument("--dense-steps", type=int, default=8)
-    ap.add_argument("--cpu-layers", type=int, default=12)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed repetitions of the K steps (the first is the headline)")
+    ap.add_argument("--stream-gib", type=float, default=2.0,
+                    help="buffer size of the read-bandwidth ceiling probe (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time one library call per step instead of a replayed HIP graph")
@@ -192,6 +195,79 @@ def dense_step_bytes(layers, B):
     return total
 
 
+# The oracle's sample of each step: (decode steps, layers) for the masked
+# decode and (steps, layers) for the dense FFN, so that the whole CPU leg takes
+# well under a minute on one core.
+CPU_SAMPLE = (2, 4, 1, 2)
+CPU_SAMPLE_BY_WORKLOAD = {"tiny_relu": (16, 2, 16, 2), "llama2_7b_reglu": (2, 8, 1, 4)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, keep, X, B, nl):
+    """The oracle as it stands, pinned to one host core in this process: the
+    masked decode (predictor, union, masked FFN, residual) over a sample of
+    steps and layers, and the dense FFN over a smaller one, both extrapolated
+    to the whole stack.  The caller's CPU affinity is restored afterwards."""
+    import numpy as np
+
+    import oracle
+    from workloads import layer_to_numpy
+    steps, nls, dsteps, dls = CPU_SAMPLE_BY_WORKLOAD.get(cfg.name, CPU_SAMPLE)
+    nls, dls = min(nls, nl), min(dls, nl)
+    host = []
+    for l in range(nls):
+        L = layer_to_numpy(keep[l])
+        L["t"] = oracle.logit_threshold(L["tau"])
+        host.append(L)
+    nproc = os.cpu_count()
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        tc = time.perf_counter()
+        for k in range(steps):
+            hh = X[k % cfg.tokens].double().cpu().numpy()
+            for L in host:
+                hh = oracle.decode_layer(L, hh, 1e-5)["h"]
+        sparse_s = time.perf_counter() - tc
+        tc = time.perf_counter()
+        for k in range(dsteps):
+            hh = X[k % cfg.tokens].double().cpu().numpy()
+            for L in host[:dls]:
+                n = np.stack([oracle.rmsnorm(v, 1e-5) for v in np.atleast_2d(hh)])
+                hh = np.atleast_2d(hh) + np.stack([oracle.ffn_dense(L, v)[0] for v in n])
+        dense_s = time.perf_counter() - tc
+        threads = len(os.sched_getaffinity(0))
+    finally:
+        os.sched_setaffinity(0, allowed)
+    per_step = sparse_s / steps * nl / nls
+    dense_per_step = dense_s / dsteps * nl / dls
+    out = {"value": round(B / per_step, 6), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"masked decode: {steps} steps (batch {B}) x {nls} of {nl} layers, "
+                     f"{sparse_s:.1f} s; dense FFN: {dsteps} steps x {dls} layers, "
+                     f"{dense_s:.1f} s; both extrapolated to {nl} layers",
+           "pinned_core": core, "host_nproc": nproc, "host_allowed_cpus": len(allowed),
+           "cpu_model": cpu_model(),
+           "ms_per_step": round(1e3 * per_step, 1),
+           "dense_ms_per_step": round(1e3 * dense_per_step, 1),
+           "dense_tokens_per_s": round(B / dense_per_step, 6),
+           "sparse_vs_dense": round(dense_per_step / per_step, 3)}
+    log(f"[cpu] 1 core ({out['cpu_model']}): masked {sparse_s:.1f}s, dense {dense_s:.1f}s -> "
+        f"{out['value']:.4f} tok/s, dense {out['dense_tokens_per_s']:.4f} tok/s")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -207,7 +283,7 @@ def main():
     import torch
 
     import activation_sparse_mlp_amd as spffn
-    from workloads import ALL, make_layer, make_profile_tokens, make_tokens
+    from workloads import ALL, make_profile_tokens, make_stack, make_tokens
 
     cfg = ALL[args.workload]
     B = args.batch
@@ -222,12 +298,13 @@ def main():
     calib = make_profile_tokens(cfg.d, args.profile_tokens, seed=1, device=dev) \
         if cfg.hot_first else None
     layers, keep = [], []
-    for l in range(nl):
-        w = make_layer(cfg, l, seed=0, device=dev, n_cal=args.n_cal)
+    n_keep = max(CPU_SAMPLE_BY_WORKLOAD.get(cfg.name, CPU_SAMPLE)[1], 1)
+    # every layer calibrated on the inputs it receives in this stack
+    for l, w in enumerate(make_stack(cfg, seed=0, device=dev, n_cal=args.n_cal, n_layers=nl)):
         if cfg.hot_first:
             w, _, _ = spffn.hot_first_permute(w, calib)
         layers.append(spffn.Layer(w))
-        keep.append(w if l < args.cpu_layers else None)
+        keep.append(w if l < n_keep else None)
         if l % 10 == 0 or l == nl - 1:
             torch.cuda.synchronize()
             log(f"[build] layer {l + 1}/{nl}  {time.time() - t0:.1f}s  "
@@ -266,20 +343,25 @@ def main():
             xbuf.copy_(X[k % cfg.tokens])
             graph.launch()
         torch.cuda.synchronize()
-    torch.cuda.synchronize()
+
+    def timed_steps(cnt_out):
+        """Exactly K steps between two synchronisations; returns elapsed ms."""
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for k in range(K):
+            if graph is None:
+                spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=cnt_out[k], ws=ws)
+            else:
+                xbuf.copy_(X[k % cfg.tokens])
+                graph.launch()
+                cnt_out[k].copy_(cbuf)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    for k in range(K):
-        if graph is None:
-            spffn.decode_step(model, X[k % cfg.tokens], h, layer_counts=counts[k], ws=ws)
-        else:
-            xbuf.copy_(X[k % cfg.tokens])
-            graph.launch()
-            counts[k].copy_(cbuf)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms = timed_steps(counts)
     wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1)
     ms_step = ms / K
     cnt = counts[:K].cpu().numpy()
     bytes_steps = [step_bytes(layers, cnt[k], B) for k in range(K)]
@@ -289,6 +371,41 @@ def main():
     active = cnt.mean() / cfg.d_ffn
     log(f"[sparse] {'eager' if graph is None else 'graph'}: {ms_step:.3f} ms/step  "
         f"{tok_s:.1f} tok/s  {gbs:.0f} GB/s  active {100 * active:.2f}%  wall {wall:.2f}s")
+
+    # Repetitions of the same K steps (the headline above is the first); their
+    # median shows how stable the figure is.
+    rep_ms = [ms_step]
+    rcounts = torch.zeros_like(counts)
+    for _ in range(args.repeats - 1):
+        rep_ms.append(timed_steps(rcounts) / K)
+    med_ms = float(np.median(rep_ms))
+    log(f"[repeats] {len(rep_ms)} x {K} steps: median {med_ms:.4f} ms/step "
+        f"(min {min(rep_ms):.4f}, max {max(rep_ms):.4f})")
+
+    # ---- validation of what was timed -------------------------------------- #
+    # (1) no down-projection workgroup gave up its bounded wait in any step so
+    #     far (a give-up would skip row reads and poison h with NaN);
+    # (2) the output is finite;
+    # (3) one graph replay equals the eager library call bit for bit on the
+    #     same token, layer counts included.
+    giveups = int(spffn.workspace_status(ws))
+    finite = bool(torch.isfinite(h).all())
+    replay_equal = True
+    if graph is not None:
+        xbuf.copy_(X[0])
+        graph.launch()
+        h_graph, c_graph = h.clone(), cbuf.clone()
+        h_eager = torch.empty_like(h)
+        c_eager = torch.empty_like(cbuf)
+        spffn.decode_step(model, X[0], h_eager, layer_counts=c_eager, ws=ws)
+        torch.cuda.synchronize()
+        replay_equal = bool(torch.equal(h_graph, h_eager) and torch.equal(c_graph, c_eager))
+    giveups = int(spffn.workspace_status(ws))  # again, after the comparison steps
+    validated = giveups == 0 and finite and replay_equal
+    log(f"[validate] give-ups {giveups}, finite {finite}, graph == eager {replay_equal}")
+    if not validated:
+        log("[validate] FAILED: the timed steps did not all do their work; no result")
+        sys.exit(3)
     del graph
 
     # ---- the dominant kernel, timed live with HIP events ------------------- #
@@ -314,6 +431,9 @@ def main():
             k_bytes.append(dominant_kernel_bytes(layers[l], kcnt[k, l], B) if B == 1
                            else batched_ffn_bytes(layers[l], kcnt[k, l], B))
     ev.close()
+    if int(spffn.workspace_status(ws)) != 0:
+        log("[validate] FAILED: a bounded wait gave up during the kernel-timing pass")
+        sys.exit(3)
     kern_us = 1e3 * float(np.mean(k_ms))
     kern_gbs = float(np.mean(k_bytes)) / (kern_us * 1e-6) / 1e9
     kern_name = ("predictor layer-2 + threshold + gate/up gather + down projection "
@@ -350,29 +470,30 @@ def main():
         log(f"[dense] {dense_ms:.3f} ms/step  {dgbs:.0f} GB/s")
         del dgraph
 
+    # ---- read ceiling: a plain streaming read over a large buffer ------------ #
+    ceiling = None
+    if args.stream_gib > 0:
+        nbytes = int(args.stream_gib * 2**30) // 16 * 16
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            spffn.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        s_ms = []
+        for _ in range(5):
+            ev0.record(stream)
+            spffn.stream_read(buf, sink)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            s_ms.append(ev0.elapsed_time(ev1))
+        del buf
+        ceiling = nbytes / (float(np.median(s_ms)) * 1e-3) / 1e9
+        log(f"[stream] read of {nbytes / 2**30:.2f} GiB: {ceiling:.0f} GB/s (median of 5)")
+
     # ---- CPU oracle on a bounded sample ------------------------------------ #
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        from workloads import layer_to_numpy
-        nc = min(args.cpu_layers, nl)
-        host = []
-        for l in range(nc):
-            L = layer_to_numpy(keep[l])
-            L["t"] = oracle.logit_threshold(L["tau"])
-            host.append(L)
-        x0 = X[0].double().cpu().numpy()
-        tc = time.perf_counter()
-        hh = x0
-        for L in host:
-            hh = oracle.decode_layer(L, hh, 1e-5)["h"]
-        el = time.perf_counter() - tc
-        per_token = el * nl / nc
-        cpu = {"value": round(B / per_token, 6), "unit": "tokens/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"1 decode step (batch {B}) through {nc} of {nl} layers, "
-                         f"{el:.1f} s single-threaded, extrapolated x{nl}/{nc} layers"}
-        log(f"[cpu] {el:.1f}s for {nc} layers -> {cpu['value']:.4f} tok/s")
+        cpu = cpu_baseline(cfg, keep, X, B, nl)
 
     out = {
         "metric": "FFN-stack decode tokens/s @batch1 + achieved HBM GB/s (% of peak) on "
@@ -396,6 +517,8 @@ def main():
             "predictor": f"{cfg.d}->{cfg.r}->{cfg.d_ffn} {cfg.p_dtype}",
             "hot_first": cfg.hot_first,
             "realised_activity": round(float(active), 5),
+            "realised_activity_layer_min": round(float(cnt.mean(axis=0).min()) / cfg.d_ffn, 5),
+            "realised_activity_layer_max": round(float(cnt.mean(axis=0).max()) / cfg.d_ffn, 5),
             "touched_bytes_per_step": int(bytes_step),
             "achieved_GBps": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
@@ -403,7 +526,18 @@ def main():
             "eager_ms_per_step": round(eager_ms, 4),
             "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 4),
             "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
+            "repeats": {"n": len(rep_ms), "steps_each": K,
+                        "ms_per_step": [round(v, 4) for v in rep_ms],
+                        "median_ms_per_step": round(med_ms, 4),
+                        "median_tokens_per_s": round(B / (med_ms * 1e-3), 3),
+                        "median_pct_of_hbm_peak": round(
+                            100 * bytes_step / (med_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)},
+            "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+            "frac_of_stream_ceiling": None if ceiling is None else round(gbs / ceiling, 4),
+            "validation": {"bounded_wait_giveups": giveups, "output_finite": finite,
+                           "graph_replay_equals_eager": replay_equal},
         },
+        "validated": validated,
         "roofline": {
             "bound": "hbm",
             "kernel": kern_name,
@@ -415,6 +549,7 @@ def main():
             "avg_launch_us": round(kern_us, 3),
             "algorithmic_bytes_per_launch": int(np.mean(k_bytes)),
             "step_achieved_GBps": round(gbs, 1),
+            "frac_of_stream_ceiling": None if ceiling is None else round(kern_gbs / ceiling, 4),
         },
         "cpu_baseline": cpu,
     }

@@ -148,9 +148,26 @@ void spffn_model_destroy(spffn_model *model);
 
 /* Bytes of device workspace that spffn_predict / spffn_forward (layer) and
  * spffn_decode_step (model) need for a batch of B tokens; 0 on bad input.
- * The workspace must be 256-byte aligned. */
+ * The workspace must be 256-byte aligned.  Its first 256 bytes are a status
+ * block (see spffn_workspace_status). */
 size_t spffn_layer_workspace_bytes(const spffn_layer *layer, int32_t B);
 size_t spffn_model_workspace_bytes(const spffn_model *model, int32_t B);
+
+/* Workspace status.  The first int32 of every workspace counts the
+ * down-projection workgroups of the single-token decode step whose bounded
+ * in-launch wait ran out (see spffn_set_wait_limit): each such workgroup wrote
+ * NaN partial sums and listed no rows, so a step with a nonzero count has a
+ * NaN output and under-reports its layer counts.  The count accumulates over
+ * every call that uses the workspace until it is cleared; a newly allocated
+ * workspace holds no meaningful count until spffn_workspace_clear_status.
+ * clear: zeroes the status block (ws_bytes >= 256), enqueued on `stream`
+ * (a fill kernel, so it may be captured into a graph).
+ * status: copies the count into *giveups (a device int32) on `stream`.
+ * SPFFN_E_ARG for NULL or misaligned pointers, SPFFN_E_WORKSPACE for a
+ * workspace smaller than its status block. */
+spffn_status spffn_workspace_clear_status(void *ws, size_t ws_bytes, void *stream);
+spffn_status spffn_workspace_status(const void *ws, size_t ws_bytes, int32_t *giveups,
+                                    void *stream);
 
 /* ---- the hot path ----------------------------------------------------- */
 
@@ -265,13 +282,25 @@ spffn_status spffn_permute_rows(const void *src, void *dst, const int32_t *perm,
 spffn_status spffn_q4_0_repack(const void *aos, void *soa, int32_t rows, int32_t cols,
                                void *stream);
 
+/* ---- measurement ------------------------------------------------------ */
+
+/* Read-bandwidth probe: reads every byte of buf [bytes] once with 16-byte
+ * non-temporal loads (the access the decode kernels use for weights) and
+ * XORs a fold of the data into *sink (a device uint32, so the loads cannot
+ * be dropped; its value has no meaning).  Timed over a buffer much larger
+ * than the caches it gives the read ceiling that the decode step's achieved
+ * bandwidth is compared with.  bytes a positive multiple of 16; buf 16-byte
+ * aligned.  SPFFN_E_ARG / SPFFN_E_SHAPE otherwise. */
+spffn_status spffn_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 /* [host] Test hook.  Inside the single-token decode step, the workgroups that
  * run a chunk's down projection wait (in the same launch) until the row groups
  * of that chunk have published their lists; the wait always ends, because
  * those row groups were dispatched before them and never wait, and it is also
  * bounded: after `polls` polls (default 2^18, far beyond any layer's run time)
  * the workgroup gives up and writes NaN partial sums, so the step yields NaN
- * instead of hanging.  polls in [0, 2^24]; 0 makes every such workgroup give
+ * instead of hanging, and it counts itself in the workspace status word
+ * (spffn_workspace_status).  polls in [0, 2^24]; 0 makes every such workgroup give
  * up at once (for testing the give-up path).  Process-wide; applies to
  * launches enqueued after the call (a captured graph keeps the value it was
  * captured with).  SPFFN_E_ARG outside the range. */

@@ -13,18 +13,25 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c to load instead (the sanitizer
+# build of the CPU tests)
+LIB = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile oracle.c with gcc (-O2, no fast-math) into liboracle.so."""
+def build(verbose: bool = False, out: str = None, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math) into liboracle.so, or with
+    AddressSanitizer and UndefinedBehaviorSanitizer into `out`."""
+    out = out or os.path.join(HERE, "liboracle.so")
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+           *(SANITIZE_FLAGS if sanitize else []), SRC, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 from .oracle import *  # noqa: E402,F401,F403

@@ -187,3 +187,27 @@ def test_set_wait_limit_range():
     assert lib.spffn_set_wait_limit(0) == OK
     assert lib.spffn_set_wait_limit(1 << 24) == OK
     assert lib.spffn_set_wait_limit(spffn.WAIT_LIMIT_DEFAULT) == OK
+
+
+def test_workspace_status_validation():
+    # host-side checks of the status calls (nothing is enqueued on failure)
+    lib = spffn.load()
+    ws = C.c_void_p(0x100000)
+    out = C.c_void_p(FAKE)
+    assert lib.spffn_workspace_clear_status(None, 4096, None) == E_ARG
+    assert lib.spffn_workspace_clear_status(C.c_void_p(0x100010), 4096, None) == E_ARG
+    assert lib.spffn_workspace_clear_status(ws, 255, None) == E_WORKSPACE
+    assert lib.spffn_workspace_status(ws, 4096, None, None) == E_ARG
+    assert lib.spffn_workspace_status(None, 4096, out, None) == E_ARG
+    assert lib.spffn_workspace_status(ws, 4096, C.c_void_p(FAKE + 2), None) == E_ARG
+    assert lib.spffn_workspace_status(ws, 100, out, None) == E_WORKSPACE
+
+
+def test_stream_read_validation():
+    lib = spffn.load()
+    x = C.c_void_p(FAKE)
+    assert lib.spffn_stream_read(None, 1024, x, None) == E_ARG
+    assert lib.spffn_stream_read(x, 1024, None, None) == E_ARG
+    assert lib.spffn_stream_read(x, 0, x, None) == E_SHAPE
+    assert lib.spffn_stream_read(x, 1000, x, None) == E_SHAPE
+    assert lib.spffn_stream_read(C.c_void_p(FAKE + 4), 1024, x, None) == E_ARG

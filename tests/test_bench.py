@@ -83,3 +83,17 @@ def test_source_hash_ignores_comments_only():
     c = "int f(int x){return x+2;}"
     assert bench.code_only(a) == bench.code_only(b)
     assert bench.code_only(b) != bench.code_only(c)
+
+
+def test_cpu_baseline_pins_one_core_and_restores_affinity():
+    from workloads import TINY, make_layer, make_tokens
+    keep = [make_layer(TINY, l, seed=0, n_cal=256) for l in range(TINY.layers)]
+    X = make_tokens(TINY.d, TINY.tokens, 1, seed=0)
+    before = os.sched_getaffinity(0)
+    out = bench.cpu_baseline(TINY, keep, X, 1, TINY.layers)
+    assert os.sched_getaffinity(0) == before
+    assert out["cores"] == 1 and out["kind"] == "oracle"
+    assert out["host_nproc"] == os.cpu_count()
+    assert out["value"] > 0 and out["dense_tokens_per_s"] > 0
+    assert isinstance(out["cpu_model"], str) and out["cpu_model"]
+    assert "16 steps" in out["sample"] and "2 of 2 layers" in out["sample"]

@@ -46,22 +46,34 @@ def test_layer_kernel_wait_gives_up_with_nan():
     # the single-token layer kernel's down-projection workgroups wait (bounded)
     # for their chunk's row groups; with a limit of 0 polls every one of them
     # gives up at once, and the step must complete with NaN rather than hang
+    # and count every give-up in the workspace status word
     cfg = _ragged("relu")
     model = _model(cfg, tau=0.5)
+    ws = model.workspace(1)  # status cleared
     x = make_tokens(cfg.d, 1, 1, seed=5, device=DEV)[0]
-    ref = spffn.decode_step(model, x)
+    ref = spffn.decode_step(model, x, ws=ws)
+    assert int(spffn.workspace_status(ws)) == 0
     torch.cuda.synchronize()
     assert torch.isfinite(ref).all()
+    counts = torch.full((2,), -1, dtype=torch.int32, device=DEV)
     try:
         spffn.set_wait_limit(0)
-        h = spffn.decode_step(model, x)
+        h = spffn.decode_step(model, x, layer_counts=counts, ws=ws)
         torch.cuda.synchronize()
     finally:
         spffn.set_wait_limit(spffn.WAIT_LIMIT_DEFAULT)
     assert torch.isnan(h).all()
-    again = spffn.decode_step(model, x)
+    gave_up = int(spffn.workspace_status(ws))
+    assert gave_up > 0  # every down-projection workgroup of both layers
+    assert np.array_equal(counts.cpu().numpy(), [0, 0])  # no chunk listed rows
+    # the count accumulates until cleared
+    again = spffn.decode_step(model, x, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(again, ref)  # bitwise: fixed summation order
+    assert int(spffn.workspace_status(ws)) == gave_up
+    spffn.workspace_clear_status(ws)
+    spffn.decode_step(model, x, ws=ws)
+    assert int(spffn.workspace_status(ws)) == 0
 
 
 def _model(cfg, tau, layers=2):
@@ -93,3 +105,23 @@ def test_no_neuron_active_keeps_residual(B):
     torch.cuda.synchronize()
     assert np.array_equal(counts.cpu().numpy(), [0, 0])
     assert torch.equal(h, x)
+
+
+@pytest.mark.parametrize("kind", ["reglu", "relu"])
+@pytest.mark.parametrize("w_dtype,d", [("f16", 12288), ("f32", 8192), ("f32", 4096)])
+def test_decode_wide_rows_single_token(kind, w_dtype, d):
+    """The single-token layer kernel with eight (fp16 d = 12288, fp32 d = 8192)
+    or four (fp32 d = 4096) packets per lane per gathered row."""
+    print(f"edge decode wide rows {kind} {w_dtype} d={d}", flush=True)
+    cfg = replace(TINY, kind=kind, w_dtype=w_dtype, p_dtype=w_dtype, d=d, d_ffn=1000, r=64,
+                  w_std=d ** -0.5)
+    _decode_checks(cfg, 1, 2, seed=57, n_cal=512)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_decode_q4_gated(B):
+    """4-bit gated rows (gate, up and down all in 4-bit blocks)."""
+    print(f"edge decode 4-bit ReGLU B={B}", flush=True)
+    from workloads import OPT_175B_Q4
+    cfg = replace(OPT_175B_Q4, kind="reglu", d=512, d_ffn=1530, r=64, layers=2)
+    _decode_checks(cfg, B, 2, seed=59, n_cal=512)

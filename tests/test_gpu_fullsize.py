@@ -1,9 +1,11 @@
 """GPU parity at the workloads' full layer shapes, in the launch configuration
 the benchmark times (decode step, hot-first rows for the 70B shape), checked
 layer by layer against the CPU oracle (teacher forced through the trace).
-Large batches are checked on sampled tokens."""
-from dataclasses import replace
-
+Stacks are generated as the benchmark generates them (make_stack: every layer
+calibrated on the inputs it receives; 4096 calibration tokens; 256 profile
+tokens for the hot-first order; the benchmark's first token), and the deep
+stacks are checked at their first, second, middle and last layers.  Large
+batches are checked on sampled tokens."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,7 @@ import activation_sparse_mlp_amd as spffn
 import oracle
 from tests.gpu_helpers import DEV, REL_L2, check_mask_agreement, np_layer, rel_l2
 from workloads import (FALCON_40B, LLAMA2_7B, LLAMA2_70B, OPT_175B_Q4, make_layer,
-                       make_profile_tokens, make_tokens)
+                       make_profile_tokens, make_stack, make_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,43 +24,58 @@ def setup_module(module):
         pytest.skip("no GPU")
 
 
-def _build(cfg, layers, hot_first, n_cal=2048):
+def teardown_function(function):
+    torch.cuda.empty_cache()
+
+
+def _build(cfg, layers, hot_first, n_cal=4096):
+    """The first `layers` layers of cfg's stack, as the benchmark builds them."""
     hosts, gl = [], []
     calib = make_profile_tokens(cfg.d, 256, seed=1, device=DEV) if hot_first else None
-    for l in range(layers):
-        w = make_layer(cfg, l, seed=0, device=DEV, n_cal=n_cal)
+    for l, w in enumerate(make_stack(cfg, seed=0, device=DEV, n_cal=n_cal, n_layers=layers)):
         if hot_first:
             w, perm, counts = spffn.hot_first_permute(w, calib)
-            c = counts.cpu().numpy()
-            assert np.array_equal(perm.cpu().numpy(), oracle.hot_first_perm(c))
+            if l < 2:
+                c = counts.cpu().numpy()
+                assert np.array_equal(perm.cpu().numpy(), oracle.hot_first_perm(c))
         gl.append(spffn.Layer(w))
         hosts.append(w)
+        if l % 16 == 15:
+            print(f"  built {l + 1}/{layers}", flush=True)
     return hosts, gl
 
 
-def _decode_check(cfg, B, layers, hot_first, tokens_checked=None):
+def _decode_check(cfg, B, layers, hot_first, tokens_checked=None, layers_checked=None):
     print(f"decode {cfg.name} B={B} layers={layers}", flush=True)
     hosts, gl = _build(cfg, layers, hot_first)
     model = spffn.Model(gl, rms_eps=1e-5)
+    ws = model.workspace(B)
     F, d = cfg.d_ffn, cfg.d
-    x = make_tokens(d, 1, B, seed=3, device=DEV)[0]
+    x = make_tokens(d, cfg.tokens, B, seed=0, device=DEV)[0]  # the benchmark's first token
     trace = dict(h_in=torch.empty(layers, B, d, device=DEV),
                  union_mask=torch.empty(layers * F, dtype=torch.uint8, device=DEV),
                  logits=torch.empty(layers * B * F, device=DEV))
     counts = torch.empty(layers, dtype=torch.int32, device=DEV)
-    h = spffn.decode_step(model, x, layer_counts=counts, trace=trace)
+    h = spffn.decode_step(model, x, layer_counts=counts, trace=trace, ws=ws)
     torch.cuda.synchronize()
+    assert int(spffn.workspace_status(ws)) == 0
+    assert torch.isfinite(h).all()
     h_in = trace["h_in"].cpu().numpy().astype(np.float64)
     outs = np.concatenate([h_in[1:], h.cpu().numpy()[None].astype(np.float64)])
     masks = trace["union_mask"].cpu().numpy().reshape(layers, F)
     lg = trace["logits"].cpu().numpy().reshape(layers, B, F)
     cnts = counts.cpu().numpy()
-    check = range(B) if tokens_checked is None else tokens_checked
+    # every layer: the count is the union's popcount, and the union is the OR
+    # of the per-token decisions on the GPU's own logits
     for l in range(layers):
+        assert cnts[l] == masks[l].sum()
+    acts = cnts / F
+    print(f"  realised activity: min {acts.min():.4f} mean {acts.mean():.4f} "
+          f"max {acts.max():.4f}", flush=True)
+    check = range(B) if tokens_checked is None else tokens_checked
+    for l in (range(layers) if layers_checked is None else layers_checked):
         L = np_layer(hosts[l])
         U = masks[l]
-        assert cnts[l] == U.sum()
-        # the union is the OR of the per-token decisions on the GPU's own logits
         assert np.array_equal(U, oracle.union(oracle.threshold(lg[l], L["t"])))
         for b in check:
             n = oracle.rmsnorm(h_in[l][b], 1e-5)
@@ -69,17 +86,34 @@ def _decode_check(cfg, B, layers, hot_first, tokens_checked=None):
             err = rel_l2(outs[l][b] - h_in[l][b], y_ref)
             print(f"  layer {l} token {b}: active {int(U.sum())}, rel-L2 {err:.2e}", flush=True)
             assert err <= REL_L2
+        del L
     # the step is bit-stable
-    h2 = spffn.decode_step(model, x)
+    h2 = spffn.decode_step(model, x, ws=ws)
     assert torch.equal(h, h2)
+    return acts
 
 
 def test_llama2_70b_decode_b1_hot_first():
     _decode_check(LLAMA2_70B, 1, 2, hot_first=True)
 
 
+@pytest.mark.timeout(600)
+def test_llama2_70b_benchmarked_stack_deep_layers():
+    """The whole 80-layer stack the benchmark times, one traced step, checked
+    at layers 0, 1, 40 and 79."""
+    acts = _decode_check(LLAMA2_70B, 1, LLAMA2_70B.layers, hot_first=True,
+                         layers_checked=[0, 1, 40, 79])
+    assert abs(acts.mean() - LLAMA2_70B.mean_activity) < 0.02
+
+
 def test_llama2_7b_decode_b1():
     _decode_check(LLAMA2_7B, 1, 2, hot_first=False)
+
+
+def test_falcon_40b_decode_b1():
+    """The non-gated fp16 single-token layer kernel at d = 8192 (12-row groups,
+    four packets per lane per gathered row)."""
+    _decode_check(FALCON_40B, 1, 2, hot_first=False)
 
 
 @pytest.mark.parametrize("B", [4, 16])
@@ -95,6 +129,17 @@ def test_opt_175b_q4_0_decode_b1():
     _decode_check(OPT_175B_Q4, 1, 1, hot_first=False)
 
 
+@pytest.mark.timeout(600)
+def test_opt_175b_q4_0_benchmarked_stack_deep_layers():
+    """The whole 96-layer 4-bit stack the benchmark times, one traced step,
+    checked at layers 0, 1, 48 and 95; every layer realises about its
+    configured 5% activity."""
+    acts = _decode_check(OPT_175B_Q4, 1, OPT_175B_Q4.layers, hot_first=False,
+                         layers_checked=[0, 1, 48, 95])
+    assert abs(acts.mean() - OPT_175B_Q4.mean_activity) < 0.01
+    assert acts.max() < 2 * OPT_175B_Q4.mean_activity
+
+
 def test_opt_175b_q4_0_forward_dense_row_sample():
     """The dense 4-bit FFN (every neuron) at full shape against the oracle on
     the same dequantised weights."""
@@ -105,7 +150,9 @@ def test_opt_175b_q4_0_forward_dense_row_sample():
     x = make_tokens(cfg.d, 1, 1, seed=4, device=DEV)[0]
     # a sampled neuron set: every 97th neuron (keeps the oracle fast)
     idx = torch.arange(0, cfg.d_ffn, 97, dtype=torch.int32, device=DEV)
+    idx_full = torch.zeros(cfg.d_ffn, dtype=torch.int32, device=DEV)
+    idx_full[:idx.numel()] = idx
     cnt = torch.tensor([idx.numel()], dtype=torch.int32, device=DEV)
-    y = spffn.forward(G, x, idx=idx, count=cnt).cpu().numpy()[0]
+    y = spffn.forward(G, x, idx=idx_full, count=cnt).cpu().numpy()[0]
     ref, _ = oracle.ffn_sparse(L, x[0].cpu().numpy(), idx.cpu().numpy())
     assert rel_l2(y, ref) <= REL_L2

@@ -112,9 +112,11 @@ def _forward_checks(cfg, B, seed=0, n_cal=1024):
     y = spffn.forward(G, xd, mask=torch.from_numpy(U).to(DEV)).cpu().numpy()
     for b in range(B):
         assert rel_l2(y[b], oracle.ffn_masked(L, xs[b], U)) <= REL_L2
-    # same set as an index list
-    idx = torch.from_numpy(oracle.compact(U)).to(DEV)
-    cnt = torch.tensor([idx.numel()], dtype=torch.int32, device=DEV)
+    # same set as an index list (in a buffer with room for d_ffn entries)
+    lst = oracle.compact(U)
+    idx = torch.zeros(cfg.d_ffn, dtype=torch.int32, device=DEV)
+    idx[:lst.size] = torch.from_numpy(lst).to(DEV)
+    cnt = torch.tensor([lst.size], dtype=torch.int32, device=DEV)
     y2 = spffn.forward(G, xd, idx=idx, count=cnt).cpu().numpy()
     assert np.array_equal(y2, y)  # same kernels, same order
     # dense

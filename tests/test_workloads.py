@@ -95,3 +95,33 @@ def test_q4_0_layer_generation():
     assert L["w_up"].dtype == torch.uint8 and L["w_up"].shape == (256, 128 // 32 * 18)
     vals = oracle.deq(L["w_up"].numpy(), "q4_0", 128)
     assert np.array_equal(vals, L["act_values"].double().numpy())
+
+
+def test_stack_keeps_configured_activity_at_depth():
+    """A stack of 4-bit ReLU layers (codes with mean -0.5 make every layer add
+    a common direction to the residual stream) realises its configured
+    activity in every layer when each layer is calibrated on the inputs it
+    receives (make_stack); the first layer is the independent layer 0."""
+    from dataclasses import replace
+
+    from workloads import OPT_175B_Q4, make_stack
+    cfg = replace(OPT_175B_Q4, d=512, d_ffn=2048, r=64, layers=6)
+    ws = list(make_stack(cfg, seed=0, n_cal=2048))
+    w0 = make_layer(cfg, 0, seed=0, n_cal=2048)
+    for k, v in w0.items():
+        if isinstance(v, torch.Tensor):
+            assert torch.equal(v, ws[0][k]), k
+    Ls = []
+    for w in ws:
+        L = layer_to_numpy(w)
+        L["t"] = oracle.logit_threshold(L["tau"])
+        Ls.append(L)
+    X = make_tokens(cfg.d, 24, 1, seed=0)
+    act = np.zeros(cfg.layers)
+    for k in range(24):
+        h = X[k].double().numpy()
+        for l, L in enumerate(Ls):
+            o = oracle.decode_layer(L, h, 1e-5)
+            act[l] += o["union"].mean() / 24
+            h = o["h"]
+    assert np.all(np.abs(act - cfg.mean_activity) < 0.015), act

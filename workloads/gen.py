@@ -17,7 +17,10 @@ Construction (one layer):
     P(w_i . x + b_i > 0) = p_i for x ~ N(0, I);
   * predictor: W1 ~ N(0, 1/d), b1 = 0; [W2 | b2] by ridge least squares of
     the true pre-activations on the hidden features over calibration tokens,
-    then b2_i shifted so that the calibration firing rate of neuron i is p_i.
+    then b2_i shifted so that the calibration firing rate of neuron i is p_i;
+  * in a stack (make_stack) every layer after the first is calibrated on the
+    normalised residual stream of the calibration tokens as the layers before
+    it leave it, with the bias from a normal fit of each pre-activation there.
 """
 import math
 
@@ -95,13 +98,18 @@ def _weights(cfg, g_codes_or_normal, g_scales, shape, device):
 
 
 def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int = 4096,
-               return_values: bool = False):
+               return_values: bool = False, cal_inputs=None):
     """One layer of `cfg` as a dict of torch tensors on `device`.
 
     Keys: kind, w_dtype, p_dtype, d, d_ffn, r, tau, w_gate (ReGLU) / None,
     w_up, w_down_t ([d_ffn, d], W_down transposed), b_act fp32 [d_ffn],
     p_w1 [r, d], p_b1 fp32 [r], p_w2 [d_ffn, r], p_b2 fp32 [d_ffn],
-    p_fire float64 numpy [d_ffn] (target firing probability per neuron)."""
+    p_fire float64 numpy [d_ffn] (target firing probability per neuron).
+
+    cal_inputs: None calibrates on fresh x ~ N(0, I) tokens (the input of a
+    first layer); or a pair (fit, shift) of [n_cal, d] fp32 tensors, the
+    normalised inputs this layer receives inside a stack (make_stack), on
+    which the bias, the predictor fit and its shift are then taken."""
     dev = torch.device(device)
     d, F, r = cfg.d, cfg.d_ffn, cfg.r
     if cfg.w_dtype == "q4_0" and d % Q4_0_BLOCK:
@@ -115,16 +123,29 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
         return _weights(cfg, _gen(dev, seed, layer, tag), _gen(dev, seed, layer, tag + 40),
                         (F, d), dev)
 
+    up_vals = None
     if cfg.kind == "reglu":
         w_gate, act_vals = w(TAG_GATE)
-        w_up, _ = w(TAG_UP)
+        w_up, up_vals = w(TAG_UP)
     else:
         w_gate = None
         w_up, act_vals = w(TAG_UP)
-    w_down_t, _ = w(TAG_DOWN)
+    w_down_t, down_vals = w(TAG_DOWN)
 
-    norms = act_vals.double().norm(dim=1)
-    b_act = (norms * torch.special.ndtri(torch.from_numpy(p).to(dev))).float()
+    ppf = torch.special.ndtri(torch.from_numpy(p).to(dev))
+    zfit = None
+    if cal_inputs is None:
+        # exact for x ~ N(0, I): w_i . x ~ N(0, ||w_i||^2)
+        norms = act_vals.double().norm(dim=1)
+        b_act = (norms * ppf).float()
+    else:
+        # inside a stack the inputs are not N(0, I) (the residual stream picks
+        # up a common direction); take each pre-activation's mean and spread
+        # over the inputs this layer actually receives, as a normal fit
+        zfit = cal_inputs[0] @ act_vals.t()
+        zd = zfit.double()
+        b_act = (-zd.mean(dim=0) + zd.std(dim=0) * ppf).float()
+        del zd
 
     # predictor first layer
     w1 = torch.randn(r, d, generator=_gen(dev, seed, layer, TAG_W1), device=dev) * d ** -0.5
@@ -133,10 +154,13 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
     b1 = torch.zeros(r, device=dev)
 
     # second layer fitted on calibration tokens
-    xc = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_CAL), device=dev)
+    if cal_inputs is None:
+        xc = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_CAL), device=dev)
+    else:
+        xc = cal_inputs[0]
     hcal = torch.relu(xc @ w1.float().t() + b1)
-    zcal = xc @ act_vals.t() + b_act
-    del xc
+    zcal = (xc @ act_vals.t() if zfit is None else zfit) + b_act
+    del xc, zfit
     ha = torch.cat([hcal, torch.ones(n_cal, 1, device=dev)], dim=1).double()
     A = ha.t() @ ha
     lam = 1e-3 * float(torch.trace(A[:r, :r])) / r
@@ -151,7 +175,10 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
     # the per-neuron shift is taken on held-out tokens: the fit's own tokens have
     # less residual variance than new ones, which would bias every rate upward
     del hcal
-    xq = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_SHIFT), device=dev)
+    if cal_inputs is None:
+        xq = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_SHIFT), device=dev)
+    else:
+        xq = cal_inputs[1]
     hq = torch.relu(xq @ w1.float().t() + b1)
     del xq
     lcal = hq @ w2.float().t() + b2                  # [n_cal, F]
@@ -174,7 +201,55 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
                p_w2=w2.contiguous(), p_b2=b2.contiguous(), p_fire=p)
     if return_values:
         out["act_values"] = act_vals
+        out["up_values"] = up_vals
+        out["down_values"] = down_vals
     return out
+
+
+def _rms(h, eps=1e-5):
+    return h * torch.rsqrt((h * h).mean(dim=1, keepdim=True) + eps)
+
+
+def _carry(w, n):
+    """What a layer adds to the residual stream of calibration inputs n
+    [N, d]: its FFN over the neurons its own predictor selects (fp32; the
+    generator's propagation only, never an expected value)."""
+    z = n @ w["act_values"].t() + w["b_act"]
+    a = torch.relu(z)
+    del z
+    if w["kind"] == "reglu":
+        a = a * (n @ w["up_values"].t())
+    hid = torch.relu(n @ w["p_w1"].float().t() + w["p_b1"])
+    logit = hid @ w["p_w2"].float().t() + w["p_b2"]
+    del hid
+    t = math.log(w["tau"] / (1.0 - w["tau"]))
+    a = torch.where(logit > t, a, torch.zeros((), device=a.device))
+    del logit
+    return a @ w["down_values"]
+
+
+def make_stack(cfg: Config, seed: int = 0, device="cpu", n_cal: int = 4096, n_layers=None):
+    """Layers 0 .. n_layers-1 of `cfg`, yielded in order, each calibrated on
+    the inputs it receives in the stack: two sets of n_cal calibration tokens
+    (x ~ N(0, I), the same draws the first layer calibrates on) are carried
+    through every layer before it -- gainless RMS norm, the layer's FFN over
+    its predicted neurons, residual add -- and their normalised values are that
+    layer's calibration inputs.  The first layer is make_layer(cfg, 0)."""
+    dev = torch.device(device)
+    n_layers = cfg.layers if n_layers is None else n_layers
+    hs = [torch.randn(n_cal, cfg.d, generator=_gen(dev, seed, 0, tag), device=dev)
+          for tag in (TAG_CAL, TAG_SHIFT)]
+    for l in range(n_layers):
+        ns = [_rms(h) for h in hs]
+        w = make_layer(cfg, l, seed=seed, device=dev, n_cal=n_cal, return_values=True,
+                       cal_inputs=None if l == 0 else ns)
+        if l + 1 < n_layers:
+            for h, n in zip(hs, ns):
+                h += _carry(w, n)
+        del ns
+        for k in ("act_values", "up_values", "down_values"):
+            w.pop(k)
+        yield w
 
 
 def make_tokens(d: int, T: int, B: int, seed: int = 0, device="cpu", tag: int = TAG_TOKENS):
