@@ -63,6 +63,7 @@ SIGNATURES = {
                                  _vp]),
     "spffn_decode_graph_create": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz,
                                          C.POINTER(_vp)]),
+    "spffn_decode_step_noalloc": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "spffn_graph_launch": (_i32, [_vp, _vp]),
     "spffn_graph_destroy": (None, [_vp]),
     "spffn_profile": (_i32, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -426,6 +427,26 @@ def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws
                                     DECODE_DENSE if dense else 0, _ptr(layer_counts),
                                     C.byref(tr) if tr is not None else None, _ptr(ws), nb,
                                     _stream()), "spffn_decode_step")
+    return h
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_step_noalloc(model, x, h=None, dense=False, layer_counts=None):
+    """decode_step with the library's static scratch array as its workspace
+    (no allocation in the library; h is allocated here only when not given)."""
+    B = _tokens(x, model.d)
+    _size(h, B * model.d, "h")
+    _size(layer_counts, model.n_layers, "layer_counts", at_least=True)
+    x = _dev(x, torch.float32, "x")
+    if h is None:
+        h = torch.empty_like(x)
+    _dev(h, torch.float32, "h", B * model.d)
+    _dev(layer_counts, torch.int32, "layer_counts", model.n_layers, at_least=True)
+    _check(load().spffn_decode_step_noalloc(model.handle, _ptr(x), _ptr(h), B,
+                                            DECODE_DENSE if dense else 0, _ptr(layer_counts),
+                                            _stream()), "spffn_decode_step_noalloc")
     return h
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -624,15 +625,22 @@ void spffn_graph_destroy(spffn_graph *graph) {
 
 namespace {
 
-spffn_status check_decode(const spffn_model *model, const float *x, const float *h, int32_t B,
-                          int32_t flags, const int32_t *layer_counts, const void *ws,
-                          size_t ws_bytes) {
+spffn_status check_decode_args(const spffn_model *model, const float *x, const float *h,
+                               int32_t B, int32_t flags, const int32_t *layer_counts) {
     if (!model || !x || !h) return fail(SPFFN_E_ARG, "decode_step: NULL model, x or h");
     spffn_status st = check_batch(B);
     if (st) return st;
     if (flags & ~SPFFN_DECODE_DENSE) return fail(SPFFN_E_ARG, "decode_step: unknown flags");
     if (!aligned(x, 16) || !aligned(h, 16) || (layer_counts && !aligned(layer_counts, 4)))
         return fail(SPFFN_E_ARG, "decode_step: x and h must be 16-byte aligned");
+    return SPFFN_OK;
+}
+
+spffn_status check_decode(const spffn_model *model, const float *x, const float *h, int32_t B,
+                          int32_t flags, const int32_t *layer_counts, const void *ws,
+                          size_t ws_bytes) {
+    spffn_status st = check_decode_args(model, x, h, B, flags, layer_counts);
+    if (st) return st;
     return check_ws(spffn_model_workspace_bytes(model, B), ws, ws_bytes);
 }
 
@@ -787,3 +795,56 @@ spffn_status spffn_q4_0_repack(const void *aos, void *soa, int32_t rows, int32_t
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode step without a caller workspace.  Its kernels use this file-scope
+// array instead: one copy per GPU, held until the process ends.  In host code
+// the name `scratch` is only a stand-in for the symbol; the array's device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SPFFN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+spffn_status scratch_address(void **out) {
+    int dev = -1;
+    SPFFN_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(SPFFN_E_ARG, "decode_step_noalloc: device %d outside [0, %d)", dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SPFFN_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return SPFFN_OK;
+}
+
+}  // namespace
+
+extern "C" spffn_status spffn_decode_step_noalloc(const spffn_model *model, const float *x,
+                                                  float *h, int32_t B, int32_t flags,
+                                                  int32_t *layer_counts, void *stream) {
+    spffn_status st = check_decode_args(model, x, h, B, flags, layer_counts);
+    if (st) return st;
+    const size_t need = spffn_model_workspace_bytes(model, B);
+    if (need > (size_t)SPFFN_NOALLOC_SCRATCH_BYTES)
+        return fail(SPFFN_E_WORKSPACE,
+                    "decode_step_noalloc: this model needs %zu bytes of scratch at B=%d, more "
+                    "than the library's static %zu-byte array (use spffn_decode_step with a "
+                    "workspace)",
+                    need, B, (size_t)SPFFN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws))) return st;
+    return enqueue_decode(model, x, h, B, flags, layer_counts, nullptr, ws, (hipStream_t)stream);
+}

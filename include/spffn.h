@@ -228,6 +228,27 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
                                int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * decode step as spffn_decode_step (same arguments and results, no trace),
+ * with the kernels' workspace taken from a static device array of the
+ * library instead of a caller buffer.  The array holds
+ * SPFFN_NOALLOC_SCRATCH_BYTES (64 MiB, enough for every shape here up to
+ * d = 12288, d_ffn = 49152 at B = 16); each GPU the library runs on keeps its
+ * own copy until the process ends.  The call allocates nothing: its first call
+ * on a device looks up that device's copy (hipGetSymbolAddress) and keeps the
+ * address.  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents, so calls that overlap on one GPU (two streams, or a call
+ * and a replay still in flight) race.  The give-up count of the bounded waits
+ * (spffn_workspace_status) is not observable here; a give-up still shows as
+ * NaN in h.  SPFFN_E_WORKSPACE when the model needs more scratch than the
+ * array holds at this B (spffn_model_workspace_bytes); otherwise errors as
+ * spffn_decode_step. */
+#define SPFFN_NOALLOC_SCRATCH_BYTES (64u << 20)
+spffn_status spffn_decode_step_noalloc(const spffn_model *model, const float *x, float *h,
+                                       int32_t B, int32_t flags, int32_t *layer_counts,
+                                       void *stream);
+
 typedef struct spffn_graph spffn_graph; /* [host] opaque: a captured decode step */
 
 /* Capture one spffn_decode_step (same arguments, no trace) into a HIP graph

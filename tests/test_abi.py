@@ -211,3 +211,24 @@ def test_stream_read_validation():
     assert lib.spffn_stream_read(x, 0, x, None) == E_SHAPE
     assert lib.spffn_stream_read(x, 1000, x, None) == E_SHAPE
     assert lib.spffn_stream_read(C.c_void_p(FAKE + 4), 1024, x, None) == E_ARG
+
+
+def test_decode_noalloc_rejects_models_beyond_its_array():
+    # host-side check, before any HIP call: a model whose workspace exceeds
+    # the library's static scratch array is refused with a clear message
+    lib = spffn.load()
+    st, h = create(d=8192, d_ffn=1 << 20, r=1024)
+    assert st == OK
+    m = C.c_void_p()
+    arr = (C.c_void_p * 1)(h.value)
+    assert lib.spffn_model_create(arr, 1, 1e-5, C.byref(m)) == OK
+    assert lib.spffn_model_workspace_bytes(m, 1) > spffn._lib.NOALLOC_SCRATCH_BYTES
+    x = C.c_void_p(FAKE)
+    assert lib.spffn_decode_step_noalloc(m, x, x, 1, 0, None, None) == E_WORKSPACE
+    assert b"static" in lib.spffn_last_error()
+    # argument checks come first, as in spffn_decode_step
+    assert lib.spffn_decode_step_noalloc(m, x, x, 0, 0, None, None) == E_SHAPE
+    assert lib.spffn_decode_step_noalloc(m, x, x, 1, 4, None, None) == E_ARG
+    assert lib.spffn_decode_step_noalloc(None, x, x, 1, 0, None, None) == E_ARG
+    lib.spffn_model_destroy(m)
+    lib.spffn_layer_destroy(h)
