@@ -64,6 +64,9 @@ SIGNATURES = {
     "spffn_decode_graph_create": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz,
                                          C.POINTER(_vp)]),
     "spffn_decode_step_noalloc": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
+    "spffn_tau_threshold": (_f32, [_f32]),
+    "spffn_decode_step_adaptive": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, C.POINTER(Trace), _vp,
+                                          _sz, _vp]),
     "spffn_graph_launch": (_i32, [_vp, _vp]),
     "spffn_graph_destroy": (None, [_vp]),
     "spffn_profile": (_i32, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -392,7 +395,23 @@ def forward(layer, x, mask=None, idx=None, count=None, y=None, ws=None):
     return y
 
 
-def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws=None):
+def tau_threshold(tau):
+    """The binary32 logit threshold ln(tau / (1 - tau)) a layer of this tau uses."""
+    return float(load().spffn_tau_threshold(float(tau)))
+
+
+def decode_step_adaptive(model, x, thresholds, h=None, layer_counts=None, trace=None, ws=None):
+    """decode_step with a logit threshold per layer and token: thresholds is a
+    device fp32 tensor [L, B] (tau_threshold of each per-token tau)."""
+    B = _tokens(x, model.d)
+    _size(thresholds, model.n_layers * B, "thresholds")
+    thresholds = _dev(thresholds, torch.float32, "thresholds", model.n_layers * B)
+    return decode_step(model, x, h=h, layer_counts=layer_counts, trace=trace, ws=ws,
+                       _thresholds=thresholds)
+
+
+def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws=None,
+                _thresholds=None):
     """One pass of the whole stack: returns h [B, d].  `trace` is an optional
     dict with device tensors h_in [L, B, d] f32, union_mask [sum d_ffn] u8,
     logits [sum B*d_ffn] f32, and `events`, a ctypes array of 2L hipEvent_t
@@ -423,10 +442,16 @@ def decode_step(model, x, h=None, dense=False, layer_counts=None, trace=None, ws
                    events=None if ev is None else C.cast(ev, C.c_void_p))
     ws = model.workspace(B) if ws is None else ws
     nb = _ws_bytes(ws, model.workspace_bytes(B))
+    trp = C.byref(tr) if tr is not None else None
+    if _thresholds is not None:
+        _check(load().spffn_decode_step_adaptive(model.handle, _ptr(x), _ptr(h), B,
+                                                 _ptr(_thresholds), _ptr(layer_counts), trp,
+                                                 _ptr(ws), nb, _stream()),
+               "spffn_decode_step_adaptive")
+        return h
     _check(load().spffn_decode_step(model.handle, _ptr(x), _ptr(h), B,
-                                    DECODE_DENSE if dense else 0, _ptr(layer_counts),
-                                    C.byref(tr) if tr is not None else None, _ptr(ws), nb,
-                                    _stream()), "spffn_decode_step")
+                                    DECODE_DENSE if dense else 0, _ptr(layer_counts), trp,
+                                    _ptr(ws), nb, _stream()), "spffn_decode_step")
     return h
 
 

@@ -186,12 +186,13 @@ spffn_status run_ffn(const Layer &L, const float *x, const float *scale, int B,
 // 1 and stored per token to w.tsc.
 spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, float eps,
                          float *logits, uint8_t *mask, uint8_t *uni, const Ws &w, hipStream_t s,
-                         bool split_ready = false, bool tiles = false, bool raw = false) {
+                         bool split_ready = false, bool tiles = false, bool raw = false,
+                         const float *tvec = nullptr) {
     const spffn_layer_desc &D = L.desc;
     if (single(L, B)) {
         SPFFN_HIP(launch_w1_b1(L, x, eps, normalize, w.hid, w.scale, s), "predictor layer-1 launch");
         uint8_t *m = mask ? mask : uni;
-        SPFFN_HIP(launch_w2_b1(L, w.hid, logits, m, s), "predictor layer-2 launch");
+        SPFFN_HIP(launch_w2_b1(L, w.hid, logits, m, tvec, s), "predictor layer-2 launch");
         if (mask && uni)
             SPFFN_HIP(hipMemcpyAsync(uni, mask, D.d_ffn, hipMemcpyDeviceToDevice, s), "union copy");
         return SPFFN_OK;
@@ -202,7 +203,7 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
                       "split launch");
         SPFFN_HIP(launch_mfma_predict(L, w.xhi, w.xlo, B, w.w1p, w.hid, w.hhi, w.hlo, logits, mask,
                                       uni, tiles ? w.tmask : nullptr, raw ? w.ss : nullptr, eps,
-                                      raw ? w.tsc : nullptr, s),
+                                      raw ? w.tsc : nullptr, tvec, s),
                   "batched predictor launch");
         return SPFFN_OK;
     }
@@ -213,8 +214,8 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
     }
     SPFFN_HIP(launch_gemv_hid(D.p_dtype, L.w1, D.r, D.d, xin, B, D.p_b1, w.hid, s),
               "predictor layer-1 launch");
-    SPFFN_HIP(launch_gemv_mask(D.p_dtype, L.w2, D.d_ffn, D.r, w.hid, B, D.p_b2, L.t, logits, mask,
-                               uni, s),
+    SPFFN_HIP(launch_gemv_mask(D.p_dtype, L.w2, D.d_ffn, D.r, w.hid, B, D.p_b2, L.t, tvec, logits,
+                               mask, uni, s),
               "predictor layer-2 launch");
     return SPFFN_OK;
 }
@@ -308,7 +309,7 @@ namespace {
 //      which also clears the chunk counters for the next layer.
 spffn_status decode_one_token(const spffn_model *model, const float *x, float *h,
                               int32_t *layer_counts, const spffn_trace *trace, void *ws,
-                              hipStream_t s) {
+                              const float *tvec, hipStream_t s) {
     const int d = model->d;
     if (x != h) SPFFN_HIP(launch_copy_words(x, h, d, s), "input copy launch");
     {
@@ -335,7 +336,8 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
         const int chunks = fused_chunks(L);
         int32_t *lc = layer_counts ? layer_counts + l : nullptr;
         SPFFN_HIP(launch_layer_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, w.done, w.part,
-                                  lc ? w.gcnt : nullptr, w.status, s, e0, e1),
+                                  lc ? w.gcnt : nullptr, w.status, tvec ? tvec + l : nullptr, s,
+                                  e0, e1),
                   "predictor layer-2 + gather + down launch");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
@@ -356,7 +358,7 @@ spffn_status check_decode(const spffn_model *model, const float *x, const float 
                           size_t ws_bytes);
 spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, int32_t B,
                             int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
-                            void *ws, hipStream_t s);
+                            void *ws, hipStream_t s, const float *tvec = nullptr);
 
 }  // namespace
 
@@ -413,8 +415,7 @@ spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out)
     h->L.desc = D;
     if (D.kind == SPFFN_RELU) h->L.desc.w_gate = nullptr;
     // threshold on the logit: sigmoid(l) > tau  <=>  l > ln(tau / (1 - tau))
-    const double tau = (double)D.tau;
-    h->L.t = (float)std::log(tau / (1.0 - tau));
+    h->L.t = spffn_tau_threshold(D.tau);
     h->L.gate = wmat(h->L.desc.w_gate, D.w_dtype, D.d_ffn, D.d);
     h->L.up = wmat(D.w_up, D.w_dtype, D.d_ffn, D.d);
     h->L.down = wmat(D.w_down_t, D.w_dtype, D.d_ffn, D.d);
@@ -571,6 +572,25 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
     return enqueue_decode(model, x, h, B, flags, layer_counts, trace, ws, (hipStream_t)stream);
 }
 
+float spffn_tau_threshold(float tau) {
+    if (!(tau > 0.0f && tau < 1.0f)) return NAN;
+    const double t = (double)tau;
+    return (float)std::log(t / (1.0 - t));
+}
+
+spffn_status spffn_decode_step_adaptive(const spffn_model *model, const float *x, float *h,
+                                        int32_t B, const float *thresholds,
+                                        int32_t *layer_counts, const spffn_trace *trace,
+                                        void *ws, size_t ws_bytes, void *stream) {
+    if (!thresholds) return fail(SPFFN_E_ARG, "decode_step_adaptive: NULL thresholds");
+    if (!aligned(thresholds, 4))
+        return fail(SPFFN_E_ARG, "decode_step_adaptive: thresholds must be 4-byte aligned");
+    spffn_status st = check_decode(model, x, h, B, 0, layer_counts, ws, ws_bytes);
+    if (st) return st;
+    return enqueue_decode(model, x, h, B, 0, layer_counts, trace, ws, (hipStream_t)stream,
+                          thresholds);
+}
+
 struct spffn_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;
@@ -646,14 +666,14 @@ spffn_status check_decode(const spffn_model *model, const float *x, const float 
 
 spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, int32_t B,
                             int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
-                            void *ws, hipStream_t s) {
+                            void *ws, hipStream_t s, const float *tvec) {
     spffn_status st = SPFFN_OK;
     const bool dense = flags & SPFFN_DECODE_DENSE;
     const int d = model->d;
     {
         const Layer &L0 = model->layers[0]->L;
         if (B == 1 && !dense && model->uniform && single(L0, 1) && fused_fits(L0))
-            return decode_one_token(model, x, h, layer_counts, trace, ws, s);
+            return decode_one_token(model, x, h, layer_counts, trace, ws, tvec, s);
     }
     if (x != h) SPFFN_HIP(launch_copy_words(x, h, (int64_t)B * d, s), "input copy launch");
     size_t mask_off = 0, logit_off = 0;
@@ -696,7 +716,7 @@ spffn_status enqueue_decode(const spffn_model *model, const float *x, float *h, 
             // the matrix-core gather lists the union rows itself (from tile
             // masks of the predictor's last kernel); other paths compact
             if ((st = run_predict(L, xin, B, one, model->eps, lg, nullptr, w.uni, w, s, mf, mf,
-                                  chain)))
+                                  chain, tvec ? tvec + l * (size_t)B : nullptr)))
                 return st;
             if (!mf)
                 SPFFN_HIP(launch_compact(w.uni, F, w.idx, w.count, s,

@@ -63,9 +63,10 @@ hipError_t launch_q4_0_repack(const void *aos, void *soa, int rows, int cols, hi
 //   counts[i]  += #{b : W[i] . x_b + bias[i] > 0}
 hipError_t launch_gemv_hid(int fmt, WMat w, int rows, int cols, const float *x, int B,
                            const float *bias, float *out, hipStream_t s);
+// tvec (or nullptr): per-token thresholds [B] replacing t
 hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x, int B,
-                            const float *bias, float t, float *logits, uint8_t *mask,
-                            uint8_t *uni, hipStream_t s);
+                            const float *bias, float t, const float *tvec, float *logits,
+                            uint8_t *mask, uint8_t *uni, hipStream_t s);
 hipError_t launch_gemv_count(int fmt, WMat w, int rows, int cols, const float *x, int B,
                              const float *bias, int32_t *counts, hipStream_t s);
 
@@ -92,7 +93,7 @@ int down_b1_chunks(const Layer &L);
 hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
                         float *scale_out, hipStream_t s);
 hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t *mask,
-                        hipStream_t s);
+                        const float *tvec, hipStream_t s);
 hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, const int32_t *idx,
                         const int32_t *count, float *act, hipStream_t s);
 hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *count,
@@ -110,7 +111,8 @@ hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normal
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
                                float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
-                               const float *ss, float eps, float *tsc, hipStream_t s);
+                               const float *ss, float eps, float *tsc, const float *tvec,
+                               hipStream_t s);
 // tsc (or nullptr): per-token scale of the products (the RMS scale of a raw input)
 hipError_t launch_mfma_ffn(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                            const int32_t *idx, const int32_t *count, _Float16 *ahi, _Float16 *alo,
@@ -155,7 +157,7 @@ void set_chunk_wait_polls(int polls);
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
                            int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
-                           hipStream_t s, hipEvent_t ev_start = nullptr,
+                           const float *tvec, hipStream_t s, hipEvent_t ev_start = nullptr,
                            hipEvent_t ev_stop = nullptr);
 
 }  // namespace spffn

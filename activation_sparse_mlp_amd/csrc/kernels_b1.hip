@@ -131,6 +131,7 @@ template <int PF, int R>
 __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
                                                     const float *__restrict__ hid,
                                                     const float *__restrict__ b2, float t,
+                                                    const float *__restrict__ tvec,
                                                     float *__restrict__ logits,
                                                     uint8_t *__restrict__ mask) {
     constexpr int E = PacketElems<PF>::value;
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
         if (lane == 0 && row < rows) {
             const float l = v + b2[row];
             if (logits) logits[row] = l;
-            mask[row] = (uint8_t)(l > t);
+            mask[row] = (uint8_t)(l > (tvec ? tvec[0] : t));
         }
     }
 }
@@ -440,6 +441,7 @@ struct FusedArgs {
     const float *hid;     // [r]
     const float *b2;      // [d_ffn]
     float t;
+    const float *tvec;    // the token's threshold (device, replaces t), or nullptr
     const float *bias;    // [d_ffn] or nullptr
     const float *h;       // [d] residual stream (un-normalised)
     const float *scale;   // device RMS scale
@@ -499,6 +501,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         s_bias[threadIdx.x] = (a.bias && row < a.d_ffn) ? a.bias[row] : 0.0f;
     }
     const float s = *a.scale;
+    const float thr = a.tvec ? *a.tvec : a.t;
 
     // logits, threshold, mask
     uint32_t bits = 0;
@@ -513,7 +516,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         const int row = g + G * (wv + 4 * q);
         if (row < a.d_ffn) {
             const float l = v + bq;
-            const bool m = l > a.t;
+            const bool m = l > thr;
             bits |= (uint32_t)m << q;
             if (lane == 0) {
                 if (a.logits) a.logits[row] = l;
@@ -854,17 +857,17 @@ hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normaliz
 }
 
 hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t *mask,
-                        hipStream_t s) {
+                        const float *tvec, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     constexpr int R = 8;
     const int blocks = (D.d_ffn + 4 * R - 1) / (4 * R);
     const size_t lds = (size_t)D.r * 4;
     if (D.p_dtype == SPFFN_F16)
-        w2_b1_kernel<kF16, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, logits,
-                                                       mask);
+        w2_b1_kernel<kF16, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
+                                                       logits, mask);
     else
-        w2_b1_kernel<kF32, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, logits,
-                                                       mask);
+        w2_b1_kernel<kF32, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
+                                                       logits, mask);
     return hipGetLastError();
 }
 
@@ -1046,7 +1049,8 @@ static void launch_layer_kind(const FusedArgs &f, const DownListArgs &dn, bool g
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
                            int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
-                           hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                           const float *tvec, hipStream_t s, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
     const bool gated = D.kind == SPFFN_REGLU;
     const int G = fused_groups(L), UA = fused_ua(L), C = fused_chunks(L), NG = fused_per_chunk(L);
@@ -1062,6 +1066,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     f.hid = hid;
     f.b2 = D.p_b2;
     f.t = L.t;
+    f.tvec = tvec;
     f.bias = D.b_act;
     f.h = h;
     f.scale = scale;

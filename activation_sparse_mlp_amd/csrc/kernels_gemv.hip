@@ -19,6 +19,7 @@ struct GemvArgs {
     int B;
     const float *bias;  // [rows] or nullptr
     float t;
+    const float *tvec;  // kEpiMask: per-token thresholds [B] replacing t, or nullptr
     float *out;         // kEpiHid: [B, rows]
     float *logits;      // kEpiMask: [B, rows] or nullptr
     uint8_t *mask;      // kEpiMask: [B, rows] or nullptr
@@ -42,7 +43,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, const 
         for (int b = 0; b < NB; ++b) {
             if (b < a.B) {
                 const float l = v[b] + bias;
-                const uint8_t m = (uint8_t)(l > a.t);
+                const uint8_t m = (uint8_t)(l > (a.tvec ? a.tvec[b] : a.t));
                 if (a.logits) a.logits[(size_t)b * a.rows + row] = l;
                 if (a.mask) a.mask[(size_t)b * a.rows + row] = m;
                 u |= m;
@@ -234,8 +235,8 @@ hipError_t launch_gemv_hid(int fmt, WMat w, int rows, int cols, const float *x, 
 }
 
 hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x, int B,
-                            const float *bias, float t, float *logits, uint8_t *mask,
-                            uint8_t *uni, hipStream_t s) {
+                            const float *bias, float t, const float *tvec, float *logits,
+                            uint8_t *mask, uint8_t *uni, hipStream_t s) {
     GemvArgs a{};
     a.w = w;
     a.rows = rows;
@@ -244,6 +245,7 @@ hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x,
     a.B = B;
     a.bias = bias;
     a.t = t;
+    a.tvec = tvec;
     a.logits = logits;
     a.mask = mask;
     a.uni = uni;

@@ -143,6 +143,7 @@ struct BgArgs {
     // epilogues
     const float *bias;     // [rows] or nullptr (mask: b2; act: b_act)
     float t;               // mask: logit threshold
+    const float *tvec;     // mask: per-token thresholds [B] replacing t, or nullptr
     float *part;           // partial: [gridDim.y, B, rows]
     float *logits;         // mask: [B, rows] or nullptr
     uint8_t *mask;         // mask: [B, rows] or nullptr
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                 a.part[((size_t)blockIdx.y * a.B + n) * a.rows + rr] = za;
             } else if constexpr (EPI == kEpiMask) {
                 const float l = za + (a.bias ? a.bias[rr] : 0.0f);
-                const bool mk = l > a.t;
+                const bool mk = l > (a.tvec ? a.tvec[n] : a.t);
                 if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
                 if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
                 if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
@@ -668,7 +669,8 @@ static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,
                                float *w1part, float *hid, _Float16 *hhi, _Float16 *hlo,
                                float *logits, uint8_t *mask, uint8_t *uni, uint16_t *tmask,
-                               const float *ss, float eps, float *tsc, hipStream_t s) {
+                               const float *ss, float eps, float *tsc, const float *tvec,
+                               hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     BgArgs a{};
     a.wa = reinterpret_cast<const _Float16 *>(L.w1.data);
@@ -690,6 +692,7 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     b.B = B;
     b.bias = D.p_b2;
     b.t = L.t;
+    b.tvec = tvec;
     b.logits = logits;
     b.mask = mask;
     b.uni = uni;

@@ -228,6 +228,30 @@ spffn_status spffn_decode_step(const spffn_model *model, const float *x, float *
                                int32_t flags, int32_t *layer_counts, const spffn_trace *trace,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* [host] The logit threshold of a probability threshold tau in (0, 1):
+ * ln(tau / (1 - tau)) evaluated in binary64 and rounded once to binary32 (the
+ * same value a layer created with that tau compares against); NaN outside
+ * (0, 1).  Guide section 3: a neuron is predicted active when
+ * sigmoid(logit) > tau. */
+float spffn_tau_threshold(float tau);
+
+/* The decode step with a threshold per token and per layer instead of each
+ * layer's tau: thresholds [L, B] (device fp32, row-major, binary32 LOGIT
+ * thresholds, e.g. spffn_tau_threshold of a per-token tau) -- token b is
+ * predicted active on neuron i of layer l when its logit > thresholds[l*B + b]
+ * (strict; NaN logits are inactive), and each layer computes every token on
+ * the union of the batch's per-token sets, as spffn_decode_step does.  The
+ * mechanism of the Guide's "Production Engineering" section 2 (tuning
+ * predictor thresholds: adaptive dynamic thresholding, which lowers tau for
+ * sensitive tokens); the policy that picks the values is the caller's.
+ * Other arguments and errors as spffn_decode_step (flags 0); SPFFN_E_ARG for
+ * NULL or misaligned thresholds.  The array is read on the device while the
+ * step runs, so the caller keeps it unchanged until the step completes. */
+spffn_status spffn_decode_step_adaptive(const spffn_model *model, const float *x, float *h,
+                                        int32_t B, const float *thresholds,
+                                        int32_t *layer_counts, const spffn_trace *trace,
+                                        void *ws, size_t ws_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same
  * decode step as spffn_decode_step (same arguments and results, no trace),

@@ -293,17 +293,26 @@ def rmsnorm(x, eps):
     return out
 
 
-def decode_layer(layer, h, eps, mask=None):
+def decode_layer(layer, h, eps, mask=None, thresholds=None):
     """One layer of the decode step for a batch h [B, d] (binary64):
     n_b = rmsnorm(h_b); M = union over the batch of the predicted masks (or
     the given `mask`); h_b + FFN over M of n_b.
+
+    thresholds: optional per-token logit thresholds [B] (binary32 values)
+    replacing the layer's t, token b's mask being logit > thresholds[b]
+    ([Guide] "Production Engineering" section 2, adaptive dynamic
+    thresholding: tau varies by token).
 
     Returns dict(h=h_next, n=[B,d], logits=[B,d_ffn], masks=[B,d_ffn],
     union=[d_ffn], y=[B,d])."""
     h = np.atleast_2d(_x64(h))
     B = h.shape[0]
     n = np.stack([rmsnorm(h[b], eps) for b in range(B)])
-    preds = [predict(layer, n[b]) for b in range(B)]
+    if thresholds is None:
+        preds = [predict(layer, n[b]) for b in range(B)]
+    else:
+        tv = np.asarray(thresholds, np.float32).reshape(B)
+        preds = [predict(dict(layer, t=float(tv[b])), n[b]) for b in range(B)]
     logits = np.stack([p[1] for p in preds])
     masks = np.stack([p[2] for p in preds])
     U = union(masks) if mask is None else np.asarray(mask, np.uint8)
@@ -311,9 +320,11 @@ def decode_layer(layer, h, eps, mask=None):
     return dict(h=h + y, n=n, logits=logits, masks=masks, union=U, y=y)
 
 
-def decode_step(layers, x, eps):
-    """The whole stack for one batch of tokens x [B, d]: returns h [B, d]."""
+def decode_step(layers, x, eps, thresholds=None):
+    """The whole stack for one batch of tokens x [B, d]: returns h [B, d].
+    thresholds: optional per-layer, per-token logit thresholds [L, B]."""
     h = np.atleast_2d(_x64(x))
-    for L in layers:
-        h = decode_layer(L, h, eps)["h"]
+    for l, L in enumerate(layers):
+        h = decode_layer(L, h, eps, thresholds=None if thresholds is None
+                         else np.asarray(thresholds)[l])["h"]
     return h

@@ -232,3 +232,31 @@ def test_decode_noalloc_rejects_models_beyond_its_array():
     assert lib.spffn_decode_step_noalloc(None, x, x, 1, 0, None, None) == E_ARG
     lib.spffn_model_destroy(m)
     lib.spffn_layer_destroy(h)
+
+
+def test_tau_threshold_and_adaptive_validation():
+    import math
+    lib = spffn.load()
+    for tau in (0.5, 0.3, 0.75, 1e-6):
+        t32 = C.c_float(tau).value
+        assert lib.spffn_tau_threshold(tau) == C.c_float(math.log(t32 / (1.0 - t32))).value
+    for bad in (0.0, 1.0, -0.5, float("nan")):
+        assert math.isnan(lib.spffn_tau_threshold(bad))
+    st, h = create()
+    assert st == OK
+    # a layer created with tau compares against spffn_tau_threshold(tau)
+    assert lib.spffn_layer_threshold(h) == lib.spffn_tau_threshold(0.5)
+    m = C.c_void_p()
+    arr = (C.c_void_p * 1)(h.value)
+    assert lib.spffn_model_create(arr, 1, 1e-5, C.byref(m)) == OK
+    nb = lib.spffn_model_workspace_bytes(m, 2)
+    x = C.c_void_p(FAKE)
+    ws = C.c_void_p(0x100000)
+    assert lib.spffn_decode_step_adaptive(m, x, x, 2, None, None, None, ws, nb, None) == E_ARG
+    assert lib.spffn_decode_step_adaptive(m, x, x, 2, C.c_void_p(FAKE + 2), None, None, ws, nb,
+                                          None) == E_ARG
+    assert lib.spffn_decode_step_adaptive(m, x, x, 17, x, None, None, ws, nb, None) == E_SHAPE
+    assert lib.spffn_decode_step_adaptive(m, x, x, 2, x, None, None, ws, nb - 256,
+                                          None) == E_WORKSPACE
+    lib.spffn_model_destroy(m)
+    lib.spffn_layer_destroy(h)

@@ -384,6 +384,47 @@ def test_decode_layer_batch_union():
         assert np.array_equal(out["y"][b], oracle.ffn_masked(L, n, out["union"]))
 
 
+@pytest.mark.parametrize("case", [0, 1])
+def test_decode_layer_per_token_thresholds_hand(case):
+    """Per-token logit thresholds (adaptive thresholding) on the hand-derived
+    two-token example: each token's own mask, their union, and every token
+    computed on the union (golden/hand_adaptive.json)."""
+    g = load_golden("hand_adaptive.json")
+    L, _, _, _ = _hand_layer("relu")
+    c = g["cases"][case]
+    out = oracle.decode_layer(L, np.asarray(g["h"], np.float64), g["eps"],
+                              thresholds=np.asarray(c["t"], np.float32))
+    assert np.array_equal(out["logits"], np.asarray(g["logits"], np.float64))
+    assert np.array_equal(out["masks"], np.asarray(c["masks"], np.uint8))
+    assert np.array_equal(out["union"], np.asarray(c["union"], np.uint8))
+    assert np.array_equal(out["y"], np.asarray(c["y"], np.float64))
+    assert np.array_equal(out["h"], np.asarray(c["h_next"], np.float64))
+
+
+def test_decode_per_token_thresholds_reduce_to_the_layer_threshold():
+    """Thresholds all equal to the layer's own t give the plain decode bit for
+    bit; a threshold below every logit for one token makes the union all ones,
+    so every token then gets the dense FFN of its input."""
+    rng = np.random.default_rng(17)
+    L = _rand_layer(rng, "reglu", 16, 40, r=8)
+    L["t"] = float(np.float32(0.1))
+    h = rng.standard_normal((3, 16))
+    plain = oracle.decode_layer(L, h, 1e-5)
+    same = oracle.decode_layer(L, h, 1e-5, thresholds=np.full(3, L["t"], np.float32))
+    for k in ("logits", "masks", "union", "y", "h"):
+        assert np.array_equal(plain[k], same[k]), k
+    low = oracle.decode_layer(L, h, 1e-5, thresholds=np.float32([1e30, -1e30, 1e30]))
+    assert np.all(low["masks"][1] == 1) and np.all(low["masks"][0] == 0)
+    for b in range(3):
+        n = oracle.rmsnorm(h[b], 1e-5)
+        assert np.array_equal(low["y"][b], oracle.ffn_dense(L, n)[0])
+    # a stack with per-layer, per-token thresholds runs each layer with its row
+    L2 = dict(L, t=-0.3)
+    T = np.float32([[0.1, 0.1, 0.1], [-0.3, -0.3, -0.3]])
+    assert np.array_equal(oracle.decode_step([L, L2], h, 1e-5, thresholds=T),
+                          oracle.decode_step([L, L2], h, 1e-5))
+
+
 def _one_neuron_layer(v):
     """d = 4, two ReLU neurons, predictor fixed to fire neuron 0 only (zero
     weights, logit biases +5 / -5); neuron 0 reads n[0] and writes v, neuron 1
