@@ -14,11 +14,11 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspffn.so")
 
-F32, F16, Q4_0 = 0, 1, 2
+F32, F16, Q4_0, FP8_E4M3 = 0, 1, 2, 3
 RELU, REGLU = 0, 1
 MAX_BATCH = 16
 DECODE_DENSE = 1
-_DTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0}
+_DTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "fp8": FP8_E4M3}
 _KINDS = {"relu": RELU, "reglu": REGLU}
 _STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_WORKSPACE", -5: "E_HIP"}
 
@@ -190,15 +190,17 @@ class Layer:
         self.d, self.d_ffn, self.r = int(w["d"]), int(w["d_ffn"]), int(w["r"])
         self.tau = float(w["tau"])
         wd = {"f32": torch.float32, "f16": torch.float16, "q4_0": torch.uint8}[self.w_dtype]
-        pd = {"f32": torch.float32, "f16": torch.float16}[self.p_dtype]
+        pd = {"f32": torch.float32, "f16": torch.float16, "fp8": torch.uint8}[self.p_dtype]
         if min(self.d, self.d_ffn, self.r) <= 0:
             raise ValueError(f"d={self.d}, d_ffn={self.d_ffn}, r={self.r} must be positive")
         if self.w_dtype == "q4_0" and self.d % 32:
             raise ValueError(f"4-bit rows need d % 32 == 0, got d={self.d}")
         n_w = self.d_ffn * (self.d // 32 * 18 if self.w_dtype == "q4_0" else self.d)
+        # fp8 predictor matrices: the codes, then one fp32 scale per row
+        ps = 4 if self.p_dtype == "fp8" else 0
         sizes = {"w_gate": n_w, "w_up": n_w, "w_down_t": n_w, "b_act": self.d_ffn,
-                 "p_w1": self.r * self.d, "p_b1": self.r, "p_w2": self.d_ffn * self.r,
-                 "p_b2": self.d_ffn}
+                 "p_w1": self.r * (self.d + ps), "p_b1": self.r,
+                 "p_w2": self.d_ffn * (self.r + ps), "p_b2": self.d_ffn}
         for k, n in sizes.items():  # every size before any device check
             if isinstance(w.get(k), torch.Tensor) and (k != "w_gate" or self.kind == "reglu"):
                 _size(w[k], n, k)
@@ -211,8 +213,8 @@ class Layer:
         if "w_up" not in t or "w_down_t" not in t or (self.kind == "reglu" and "w_gate" not in t):
             raise ValueError("missing FFN weight (w_up, w_down_t, and w_gate for ReGLU)")
         t["b_act"] = _dev(w.get("b_act"), torch.float32, "b_act", self.d_ffn)
-        for k, n in (("p_w1", self.r * self.d), ("p_w2", self.d_ffn * self.r)):
-            t[k] = _dev(w[k], pd, k, n)
+        for k in ("p_w1", "p_w2"):
+            t[k] = _dev(w[k], pd, k, sizes[k])
         for k, n in (("p_b1", self.r), ("p_b2", self.d_ffn)):
             t[k] = _dev(w[k], torch.float32, k, n)
         self.tensors = t
@@ -595,10 +597,17 @@ def hot_first_permute(w, calib_x):
     counts = profile(layer, calib_x)
     perm = hot_first_order(counts)
     out = dict(w)
+    F = int(w["d_ffn"])
     for k in PERMUTED_KEYS:
         if w.get(k) is not None and (k != "w_gate" or w["kind"] == "reglu"):
             src = w[k]
-            if src.dim() == 1:
+            if k == "p_w2" and w["p_dtype"] == "fp8":
+                # the codes [d_ffn, r] and the per-row scales move together
+                r = int(w["r"])
+                codes = permute_rows(src[:F * r].view(F, r), perm)
+                scales = permute_rows(src[F * r:].view(F, 4), perm)
+                out[k] = torch.cat([codes.view(-1), scales.view(-1)])
+            elif src.dim() == 1:
                 out[k] = permute_rows(src.view(-1, 1), perm).view(-1)
             else:
                 out[k] = permute_rows(src, perm)

@@ -52,16 +52,23 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int elems_multiple(int dtype) { return dtype == SPFFN_F32 ? 4 : dtype == SPFFN_F16 ? 8 : 32; }
+int elems_multiple(int dtype) {
+    return dtype == SPFFN_F32 ? 4 : dtype == SPFFN_F16 ? 8 : dtype == SPFFN_FP8_E4M3 ? 16 : 32;
+}
 
 WMat wmat(const void *p, int dtype, int rows, int cols) {
     WMat w{};
     w.data = static_cast<const uint8_t *>(p);
     w.scales = nullptr;
-    w.stride = dtype == SPFFN_F32 ? (size_t)cols * 4 : dtype == SPFFN_F16 ? (size_t)cols * 2
-                                                                           : (size_t)cols / 2;
+    w.rscale = nullptr;
+    w.stride = dtype == SPFFN_F32 ? (size_t)cols * 4
+               : dtype == SPFFN_F16 ? (size_t)cols * 2
+               : dtype == SPFFN_FP8_E4M3 ? (size_t)cols
+                                         : (size_t)cols / 2;
     if (dtype == SPFFN_Q4_0 && p)
         w.scales = reinterpret_cast<const uint16_t *>(w.data + (size_t)rows * (cols / 2));
+    if (dtype == SPFFN_FP8_E4M3 && p)
+        w.rscale = reinterpret_cast<const float *>(w.data + (size_t)rows * cols);
     return w;
 }
 
@@ -386,8 +393,9 @@ spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out)
         return fail(SPFFN_E_ARG, "layer_create: unknown kind %d", D.kind);
     if (D.w_dtype != SPFFN_F32 && D.w_dtype != SPFFN_F16 && D.w_dtype != SPFFN_Q4_0)
         return fail(SPFFN_E_DTYPE, "layer_create: unknown weight dtype %d", D.w_dtype);
-    if (D.p_dtype != SPFFN_F32 && D.p_dtype != SPFFN_F16)
-        return fail(SPFFN_E_DTYPE, "layer_create: predictor dtype must be F32 or F16, got %d",
+    if (D.p_dtype != SPFFN_F32 && D.p_dtype != SPFFN_F16 && D.p_dtype != SPFFN_FP8_E4M3)
+        return fail(SPFFN_E_DTYPE,
+                    "layer_create: predictor dtype must be F32, F16 or FP8_E4M3, got %d",
                     D.p_dtype);
     if (D.d % elems_multiple(D.w_dtype))
         return fail(SPFFN_E_SHAPE, "layer_create: d=%d must be a multiple of %d for dtype %d", D.d,

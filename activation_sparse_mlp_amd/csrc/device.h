@@ -22,13 +22,19 @@ template <int FMT> struct PacketElems;
 template <> struct PacketElems<kF32> { static constexpr int value = 4; };
 template <> struct PacketElems<kF16> { static constexpr int value = 8; };
 template <> struct PacketElems<kQ4> { static constexpr int value = 32; };
+template <> struct PacketElems<kFP8> { static constexpr int value = 16; };
 
-inline int packet_elems(int fmt) { return fmt == kF32 ? 4 : fmt == kF16 ? 8 : 32; }
+inline int packet_elems(int fmt) {
+    return fmt == kF32 ? 4 : fmt == kF16 ? 8 : fmt == kFP8 ? 16 : 32;
+}
 
 // Bytes of one stored row of `cols` elements.
 template <int FMT>
 __host__ __device__ __forceinline__ size_t row_bytes(int cols) {
-    return FMT == kF32 ? (size_t)cols * 4 : FMT == kF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+    return FMT == kF32 ? (size_t)cols * 4
+           : FMT == kF16 ? (size_t)cols * 2
+           : FMT == kFP8 ? (size_t)cols
+                         : (size_t)cols / 2;
 }
 
 template <int FMT>
@@ -41,12 +47,42 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// fp8 (OCP E4M3) codes are widened as value / 256: the code's sign and its
+// seven magnitude bits are moved under the binary16 sign, exponent and
+// mantissa (E4M3 has exponent bias 7, binary16 bias 15, so every E4M3 value,
+// subnormals included, is exactly 2^8 times the binary16 value so formed;
+// the NaN codes 0x7F / 0xFF are not supported and read as +-480).  The 2^8
+// goes into the row scale, so the scale a kernel applies is rscale * 256.
+template <int FMT>
+__device__ __forceinline__ float row_scale(const WMat &w, size_t row) {
+    if constexpr (FMT == kFP8)
+        return w.rscale[row] * 256.0f;
+    else
+        return 1.0f;
+}
+
 template <int FMT>
 __device__ __forceinline__ float packet_scale(const WMat &w, size_t row, int cols, int pg) {
     if constexpr (FMT == kQ4)
         return half_bits_to_float(w.scales[row * (size_t)(cols / 32) + pg]);
+    else if constexpr (FMT == kFP8)
+        return row_scale<kFP8>(w, row);
     else
         return 1.0f;
+}
+
+// The four E4M3 codes of a 32-bit word (byte n = code n) as value / 256.
+__device__ __forceinline__ void e4m3x4_div256(uint32_t w, float (&v)[4]) {
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const uint32_t x01 = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);  // code 0 | code 1 << 16
+    const uint32_t x23 = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);  // code 2 | code 3 << 16
+    const uint32_t h01 = ((x01 & 0x007F007Fu) << 7) | ((x01 & 0x00800080u) << 8);
+    const uint32_t h23 = ((x23 & 0x007F007Fu) << 7) | ((x23 & 0x00800080u) << 8);
+    const half2v a = __builtin_bit_cast(half2v, h01), b = __builtin_bit_cast(half2v, h23);
+    v[0] = (float)a[0];
+    v[1] = (float)a[1];
+    v[2] = (float)b[0];
+    v[3] = (float)b[1];
 }
 
 // Byte n (0..3) of a 32-bit word as a float, written so that it compiles to
@@ -162,6 +198,30 @@ __device__ __forceinline__ void packet_dot(const uint4 raw, float scale, const f
             a = fmaf(w[7], v1.w, a);
             acc[b] = a;
         }
+    } else if constexpr (FMT == kFP8) {
+        // 16 codes, word m holding columns 4m..4m+3; scale = rscale * 256
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        float w[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float v4[4];
+            e4m3x4_div256(words[m], v4);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) w[4 * m + n] = v4[n];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float a = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 v = lds4(xl + b * XS, NP, g, p);
+                a = fmaf(w[4 * g + 0], v.x, a);
+                a = fmaf(w[4 * g + 1], v.y, a);
+                a = fmaf(w[4 * g + 2], v.z, a);
+                a = fmaf(w[4 * g + 3], v.w, a);
+            }
+            acc[b] = fmaf(scale, a, acc[b]);
+        }
     } else {
         // 4-bit block: word m holds codes 4m..4m+3 in its low nibbles (group m)
         // and codes 16+4m..16+4m+3 in its high nibbles (group 4+m).
@@ -243,6 +303,17 @@ __device__ __forceinline__ float packet_dot_reg(const uint4 raw, float scale,
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], xv[e], acc);
         return acc;
+    } else if constexpr (FMT == kFP8) {
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        float s = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float v4[4];
+            e4m3x4_div256(words[m], v4);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) s = fmaf(v4[n], xv[4 * m + n], s);
+        }
+        return fmaf(scale, s, acc);
     } else {
         // low nibbles as bytes (q), high nibbles in place (16 q), see packet_dot
         const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};

@@ -12,14 +12,15 @@ namespace spffn {
 constexpr int kWave = 64;
 
 // Weight storage formats.  A "packet" is the 16 bytes one lane loads at a time:
-// 4 fp32, 8 fp16, or one 4-bit block of 32 codes (whose fp16 scale lives in a
-// separate array).
-enum Fmt : int { kF32 = 0, kF16 = 1, kQ4 = 2 };
+// 4 fp32, 8 fp16, one 4-bit block of 32 codes (whose fp16 scale lives in a
+// separate array), or 16 fp8 (E4M3) codes of a row with one fp32 scale.
+enum Fmt : int { kF32 = 0, kF16 = 1, kQ4 = 2, kFP8 = 3 };
 
 // One weight matrix [rows, cols] in device memory.
 struct WMat {
-    const uint8_t *data;     // fp32/fp16 elements, or the 4-bit code region
+    const uint8_t *data;     // fp32/fp16 elements, 4-bit or fp8 code region
     const uint16_t *scales;  // 4-bit only: fp16 scale bits [rows, cols/32]
+    const float *rscale;     // fp8 only: one fp32 scale per row [rows]
     size_t stride;           // bytes from one row to the next (data region)
 };
 

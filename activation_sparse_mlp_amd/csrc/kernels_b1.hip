@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void w1_b1_kernel(WMat w1, int r, int d,
             if (p < NP) packet_dot<PF, 1>(raw[u], 1.0f, xl, NP, p, nullptr, acc);
         }
     }
-    const float v = wave_sum(acc[0]);
+    const float v = wave_sum(acc[0]) * row_scale<PF>(w1, rv ? row : 0);
     if (rv && lane == 0) hid[row] = fmaxf(fmaf(v, s, b1 ? b1[row] : 0.0f), 0.0f);
 }
 
@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
     }
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-        const float v = wave_sum(acc[q][0]);
         const int row = row0 + q;
+        const float v = wave_sum(acc[q][0]) * row_scale<PF>(w2, row < rows ? row : 0);
         if (lane == 0 && row < rows) {
             const float l = v + b2[row];
             if (logits) logits[row] = l;
@@ -458,7 +458,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
     constexpr int RB = 4 * RW;     // rows per row group (one group per workgroup)
-    constexpr int PL = 2;          // W2 packets per lane per row (rows of <= 128 packets)
+    constexpr int PL = PF == kFP8 ? 1 : 2;  // W2 packets per lane per row (one pass)
     __shared__ uint32_t s_bits[4];
     __shared__ float s_bias[RB];   // bias of every row of the group, by local index
     __shared__ float s_part[RB][4][2];
@@ -491,10 +491,12 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         float unused;
         load_packet_x<PF>(a.hid, p < NPr ? p : NPr - 1, hv[u], unused);
     }
-    float b2v;
+    float b2v, rsv;
     {
         const int row = g + G * (wv + 4 * (lane < RW ? lane : 0));
-        b2v = a.b2[row < a.d_ffn ? row : a.d_ffn - 1];
+        const int rr = row < a.d_ffn ? row : a.d_ffn - 1;
+        b2v = a.b2[rr];
+        rsv = row_scale<PF>(a.w2, rr);  // 1 except for fp8 predictor rows
     }
     if ((int)threadIdx.x < RB) {
         const int row = g + G * (int)threadIdx.x;
@@ -511,7 +513,8 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
 #pragma unroll
         for (int u = 0; u < PL; ++u)
             if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
-        const float v = wave_sum(acc);
+        const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv), q));
+        const float v = wave_sum(acc) * rq;
         const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v), q));
         const int row = g + G * (wv + 4 * q);
         if (row < a.d_ffn) {
@@ -850,6 +853,9 @@ hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normaliz
     if (D.p_dtype == SPFFN_F16)
         w1_b1_kernel<kF16><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
                                                     scale_out);
+    else if (D.p_dtype == SPFFN_FP8_E4M3)
+        w1_b1_kernel<kFP8><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
+                                                    scale_out);
     else
         w1_b1_kernel<kF32><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
                                                     scale_out);
@@ -864,6 +870,9 @@ hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t
     const size_t lds = (size_t)D.r * 4;
     if (D.p_dtype == SPFFN_F16)
         w2_b1_kernel<kF16, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
+                                                       logits, mask);
+    else if (D.p_dtype == SPFFN_FP8_E4M3)
+        w2_b1_kernel<kFP8, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
                                                        logits, mask);
     else
         w2_b1_kernel<kF32, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
@@ -1011,9 +1020,10 @@ static int fused_ua(const Layer &L) {
 }
 
 bool fused_fits(const Layer &L) {
-    // a W2 row must fit one pass of 2 packets per lane, an activated row one
-    // pass of 8 packets per lane
-    return L.desc.r / packet_elems(L.desc.p_dtype) <= 128 &&
+    // a W2 row must fit one pass of 2 packets per lane (1 for fp8 rows), an
+    // activated row one pass of 8 packets per lane
+    const int pl = L.desc.p_dtype == SPFFN_FP8_E4M3 ? 1 : 2;
+    return L.desc.r / packet_elems(L.desc.p_dtype) <= 64 * pl &&
            L.desc.d / packet_elems(L.desc.w_dtype) <= 256 * 8;
 }
 
@@ -1098,6 +1108,13 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
             launch_layer_kind<kF16, kF32>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
         else
             launch_layer_kind<kF16, kQ4>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+    } else if (D.p_dtype == SPFFN_FP8_E4M3) {
+        if (D.w_dtype == SPFFN_F16)
+            launch_layer_kind<kFP8, kF16>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else if (D.w_dtype == SPFFN_F32)
+            launch_layer_kind<kFP8, kF32>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
+        else
+            launch_layer_kind<kFP8, kQ4>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);
     } else {
         if (D.w_dtype == SPFFN_F16)
             launch_layer_kind<kF32, kF16>(f, dn, gated, slices, blocks, UA, s, ev_start, ev_stop);

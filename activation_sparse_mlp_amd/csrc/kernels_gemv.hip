@@ -218,6 +218,7 @@ template <int EPI>
 static hipError_t gemv_dispatch_fp(int fmt, GemvArgs &a, hipStream_t s) {
     if (fmt == kF32) return gemv_dispatch_nb<kF32, EPI>(a, s);
     if (fmt == kF16) return gemv_dispatch_nb<kF16, EPI>(a, s);
+    if (fmt == kFP8) return gemv_dispatch_nb<kFP8, EPI>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -78,16 +78,21 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": rows * row_bytes, "launches": 3}), flush=True)
 
 
+def pred_bytes(L):
+    """(bytes per predictor weight, bytes of per-row scale) of a layer's predictor."""
+    return {"f32": (4, 0), "f16": (2, 0), "fp8": (1, 4)}[L.p_dtype]
+
+
 def step_bytes(layers, counts, B):
     """Algorithmic bytes of one decode step from the per-layer union sizes:
     predictor weights and biases, the active rows of every FFN matrix, their
     biases and index entries, the union mask, and the activations in/out."""
     total = 0
     for L, u in zip(layers, counts):
-        wp = 4 if L.p_dtype == "f32" else 2
+        wp, ps = pred_bytes(L)
         row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
         n_mat = 3 if L.kind == "reglu" else 2
-        total += (L.r * L.d + L.d_ffn * L.r) * wp + 4 * (L.r + L.d_ffn)
+        total += (L.r * L.d + L.d_ffn * L.r) * wp + (4 + ps) * (L.r + L.d_ffn)
         total += int(u) * (n_mat * row + 4 + 4)
         total += L.d_ffn
         total += B * (2 * L.d + L.r) * 4
@@ -102,10 +107,10 @@ def dominant_kernel_bytes(L, u, B):
     down, or up and down), its bias and its list entry (index + activation),
     plus the hidden and residual vectors read.  The per-chunk partial sums it
     writes are workspace traffic, not counted."""
-    wp = 4 if L.p_dtype == "f32" else 2
+    wp, ps = pred_bytes(L)
     row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
     n_mat = 3 if L.kind == "reglu" else 2
-    return (L.d_ffn * (L.r * wp + 4 + 1) + int(u) * (n_mat * row + 4 + 8)
+    return (L.d_ffn * (L.r * wp + ps + 4 + 1) + int(u) * (n_mat * row + 4 + 8)
             + B * (L.r + L.d) * 4)
 
 

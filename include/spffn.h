@@ -63,8 +63,15 @@ typedef enum {
 typedef enum {
     SPFFN_F32 = 0,  /* IEEE binary32                                           */
     SPFFN_F16 = 1,  /* IEEE binary16                                           */
-    SPFFN_Q4_0 = 2  /* 4-bit blocks of 32 codes with an fp16 scale; on the GPU
+    SPFFN_Q4_0 = 2, /* 4-bit blocks of 32 codes with an fp16 scale; on the GPU
                        in the split layout written by spffn_q4_0_repack       */
+    SPFFN_FP8_E4M3 = 3 /* predictor weights only: OCP 8-bit floating point E4M3
+                       (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+                       no infinities) codes with one fp32 scale per row:
+                       weight[i][k] = e4m3(code[i][k]) * scale[i].  A matrix
+                       [rows, cols] is one buffer: the codes, row-major, one
+                       byte each, then the rows' fp32 scales.  The NaN codes
+                       0x7F and 0xFF must not occur.                           */
 } spffn_dtype;
 
 typedef enum {
@@ -87,9 +94,12 @@ typedef enum {
  *             t = ln(tau / (1 - tau)) computed once in binary64 and rounded to
  *             binary32 (sigmoid is increasing)
  * FFN weights are w_dtype (F32, F16 or Q4_0 split layout); predictor weights
- * are p_dtype (F32 or F16).  Shapes: F32 needs d % 4 == 0, F16 d % 8 == 0,
- * Q4_0 d % 32 == 0; the predictor needs d and r multiples of 4 (F32) or 8
- * (F16).  Every weight pointer must be 16-byte aligned. */
+ * are p_dtype (F32, F16 or FP8_E4M3: the x64 page's list item 2 and the
+ * Guide's section 3 describe a small, low-rank predictor; 8-bit weights halve
+ * its bytes, which are a third to four fifths of a decode step's).  Shapes:
+ * F32 needs d % 4 == 0, F16 d % 8 == 0, Q4_0 d % 32 == 0; the predictor needs
+ * d and r multiples of 4 (F32), 8 (F16) or 16 (FP8_E4M3).  Every weight
+ * pointer must be 16-byte aligned. */
 typedef struct {
     int32_t d, d_ffn, r;
     int32_t kind;     /* spffn_kind  */

@@ -22,10 +22,12 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #define OR_F32 0
 #define OR_F16 1
 #define OR_Q4_0 2
+#define OR_FP8_E4M3 3
 
 #define OR_RELU 0
 #define OR_REGLU 1
@@ -63,8 +65,32 @@ static double q4_0_value(const uint8_t *blk, int k)
     return (double)(q - 8) * oracle_f16_to_f64(sbits);
 }
 
-/* Row `row` of a [rows, cols] weight matrix stored as `dtype`, widened to fp64. */
-int oracle_deq_row(const void *w, int dtype, int64_t cols, int64_t row, double *out)
+/* OCP 8-bit floating point, E4M3 format (the OCP 8-bit Floating Point
+ * Specification): bit 7 is the sign, bits 6..3 the exponent e with bias 7,
+ * bits 2..0 the mantissa m.  e = 0 holds zero and the subnormals m * 2^-9;
+ * otherwise the value is (1 + m/8) * 2^(e-7); the format has no infinities and
+ * S.1111.111 is NaN (so the largest finite magnitude is 1.75 * 2^8 = 448). */
+double oracle_e4m3_to_f64(uint8_t c)
+{
+    int sign = c >> 7;
+    int e = (c >> 3) & 0xf;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* Row `row` of a [rows, cols] weight matrix stored as `dtype`, widened to fp64.
+ * An fp8 (E4M3) matrix is one buffer: rows * cols code bytes, row-major, then
+ * one fp32 scale per row; weight (i, k) = e4m3(code[i][k]) * scale[i], exact
+ * in fp64 (a 4-bit significand times a 24-bit one). */
+int oracle_deq_row(const void *w, int dtype, int64_t rows, int64_t cols, int64_t row,
+                   double *out)
 {
     int64_t k;
     if (dtype == OR_F32) {
@@ -75,6 +101,12 @@ int oracle_deq_row(const void *w, int dtype, int64_t cols, int64_t row, double *
         const uint16_t *p = (const uint16_t *)w + row * cols;
         for (k = 0; k < cols; ++k)
             out[k] = oracle_f16_to_f64(p[k]);
+    } else if (dtype == OR_FP8_E4M3) {
+        const uint8_t *p = (const uint8_t *)w + row * cols;
+        float scale;
+        memcpy(&scale, (const uint8_t *)w + rows * cols + row * 4, sizeof scale);
+        for (k = 0; k < cols; ++k)
+            out[k] = oracle_e4m3_to_f64(p[k]) * (double)scale;
     } else if (dtype == OR_Q4_0) {
         if (cols % Q4_0_BLOCK)
             return -1;
@@ -118,7 +150,7 @@ int oracle_predict(int64_t d, int64_t d_ffn, int64_t r, int p_dtype,
         return -2;
     }
     for (j = 0; j < r; ++j) {
-        if (oracle_deq_row(W1, p_dtype, d, j, row)) {
+        if (oracle_deq_row(W1, p_dtype, r, d, j, row)) {
             free(row);
             free(hid);
             return -1;
@@ -129,7 +161,7 @@ int oracle_predict(int64_t d, int64_t d_ffn, int64_t r, int p_dtype,
             hid_out[j] = hid[j];
     }
     for (i = 0; i < d_ffn; ++i) {
-        oracle_deq_row(W2, p_dtype, r, i, row);
+        oracle_deq_row(W2, p_dtype, d_ffn, r, i, row);
         double l = dot(row, hid, r) + (double)b2[i];
         if (logits)
             logits[i] = l;
@@ -179,18 +211,18 @@ void oracle_union(const uint8_t *masks, int64_t B, int64_t n, uint8_t *out)
  *   ReLU  (non-gated):  z_i = W_up[i] . x + b_i,   u_i = 1 (unused)
  *   ReGLU (gated):      z_i = W_gate[i] . x + b_i, u_i = W_up[i] . x
  * The activation is a_i = max(z_i, 0) (ReLU) or max(z_i, 0) * u_i (ReGLU). */
-static double neuron_act(int kind, int w_dtype, int64_t d,
+static double neuron_act(int kind, int w_dtype, int64_t d, int64_t d_ffn,
                          const void *W_gate, const void *W_up, const float *b,
                          const double *x, int64_t i, double *row, double *z_out)
 {
     double z, u = 1.0;
     if (kind == OR_REGLU) {
-        oracle_deq_row(W_gate, w_dtype, d, i, row);
+        oracle_deq_row(W_gate, w_dtype, d_ffn, d, i, row);
         z = dot(row, x, d) + (b ? (double)b[i] : 0.0);
-        oracle_deq_row(W_up, w_dtype, d, i, row);
+        oracle_deq_row(W_up, w_dtype, d_ffn, d, i, row);
         u = dot(row, x, d);
     } else {
-        oracle_deq_row(W_up, w_dtype, d, i, row);
+        oracle_deq_row(W_up, w_dtype, d_ffn, d, i, row);
         z = dot(row, x, d) + (b ? (double)b[i] : 0.0);
     }
     if (z_out)
@@ -228,11 +260,11 @@ int oracle_ffn_dense(int kind, int w_dtype, int64_t d, int64_t d_ffn,
         return -2;
     }
     for (i = 0; i < d_ffn; ++i)
-        a[i] = neuron_act(kind, w_dtype, d, W_gate, W_up, b, x, i, row, NULL);
+        a[i] = neuron_act(kind, w_dtype, d, d_ffn, W_gate, W_up, b, x, i, row, NULL);
     for (k = 0; k < d; ++k)
         y[k] = 0.0;
     for (i = 0; i < d_ffn; ++i) {
-        oracle_deq_row(W_downT, w_dtype, d, i, row);
+        oracle_deq_row(W_downT, w_dtype, d_ffn, d, i, row);
         for (k = 0; k < d; ++k)
             y[k] += a[i] * row[k];
         if (act)
@@ -266,8 +298,8 @@ int64_t oracle_ffn_sparse(int kind, int w_dtype, int64_t d, int64_t d_ffn,
         y[k] = 0.0;
     for (j = 0; j < count; ++j) {
         int64_t i = idx[j];
-        double a = neuron_act(kind, w_dtype, d, W_gate, W_up, b, x, i, row, NULL);
-        oracle_deq_row(W_downT, w_dtype, d, i, row);
+        double a = neuron_act(kind, w_dtype, d, d_ffn, W_gate, W_up, b, x, i, row, NULL);
+        oracle_deq_row(W_downT, w_dtype, d_ffn, d, i, row);
         for (k = 0; k < d; ++k)
             y[k] += a * row[k];
         if (act)
@@ -308,14 +340,14 @@ int oracle_preact(int kind, int w_dtype, int64_t d, int64_t d_ffn,
     for (i = 0; i < d_ffn; ++i) {
         double zi;
         if (kind == OR_REGLU) {
-            oracle_deq_row(W_gate, w_dtype, d, i, row);
+            oracle_deq_row(W_gate, w_dtype, d_ffn, d, i, row);
             zi = dot(row, x, d) + (b ? (double)b[i] : 0.0);
             if (u) {
-                oracle_deq_row(W_up, w_dtype, d, i, row);
+                oracle_deq_row(W_up, w_dtype, d_ffn, d, i, row);
                 u[i] = dot(row, x, d);
             }
         } else {
-            oracle_deq_row(W_up, w_dtype, d, i, row);
+            oracle_deq_row(W_up, w_dtype, d_ffn, d, i, row);
             zi = dot(row, x, d) + (b ? (double)b[i] : 0.0);
             if (u)
                 u[i] = 1.0;
@@ -344,7 +376,7 @@ int oracle_profile(int kind, int w_dtype, int64_t d, int64_t d_ffn,
         return -2;
     for (i = 0; i < d_ffn; ++i) {
         int32_t c = 0;
-        oracle_deq_row(W_act, w_dtype, d, i, row);
+        oracle_deq_row(W_act, w_dtype, d_ffn, d, i, row);
         for (t = 0; t < N; ++t) {
             double z = dot(row, X + t * d, d) + (b ? (double)b[i] : 0.0);
             c += (z > 0.0);

@@ -4,7 +4,7 @@ A layer is a plain dict of numpy arrays and ints:
 
   kind      "relu" (non-gated up/down) or "reglu" (gated)
   w_dtype   "f32" | "f16" | "q4_0"   storage of w_gate / w_up / w_down_t
-  p_dtype   "f32" | "f16"            storage of p_w1 / p_w2
+  p_dtype   "f32" | "f16" | "fp8"    storage of p_w1 / p_w2
   d, d_ffn, r
   w_gate    [d_ffn, d]  (ReGLU only; None for ReLU)
   w_up      [d_ffn, d]
@@ -16,7 +16,8 @@ A layer is a plain dict of numpy arrays and ints:
             when its logit is > t
 
 fp16 arrays are numpy float16; 4-bit arrays are uint8 [rows, cols/32*18] in
-the 18-byte block layout described in oracle.c.
+the 18-byte block layout described in oracle.c; fp8 (OCP E4M3) matrices are a
+flat uint8 buffer of rows*cols codes followed by rows fp32 scales.
 
 Sources (page titles abbreviated): [Guide] "PowerInfer Guide: Exploiting
 Activation Sparsity for LLM AI"; [x64] "PowerInfer_x64: Neuron-Level Sparse
@@ -30,7 +31,7 @@ import numpy as np
 
 from . import LIB, build
 
-_DT = {"f32": 0, "f16": 1, "q4_0": 2}
+_DT = {"f32": 0, "f16": 1, "q4_0": 2, "fp8": 3}
 _KIND = {"relu": 0, "reglu": 1}
 
 _lib = None
@@ -45,7 +46,9 @@ def _load():
         vp, i64, i32, dp = C.c_void_p, C.c_int64, C.c_int, C.c_double
         lib.oracle_f16_to_f64.argtypes = [C.c_uint16]
         lib.oracle_f16_to_f64.restype = dp
-        lib.oracle_deq_row.argtypes = [vp, i32, i64, i64, vp]
+        lib.oracle_e4m3_to_f64.argtypes = [C.c_uint8]
+        lib.oracle_e4m3_to_f64.restype = dp
+        lib.oracle_deq_row.argtypes = [vp, i32, i64, i64, i64, vp]
         lib.oracle_deq_row.restype = i32
         lib.oracle_predict.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, dp, vp, vp, vp]
         lib.oracle_predict.restype = i32
@@ -102,14 +105,23 @@ def f16_bits_to_f64(bits):
     return out.reshape(np.shape(bits))
 
 
+def e4m3_to_f64(codes):
+    """OCP E4M3 codes (uint8 array) -> float64, one C call per value."""
+    lib = _load()
+    flat = np.asarray(codes, dtype=np.uint8).ravel()
+    out = np.array([lib.oracle_e4m3_to_f64(int(c)) for c in flat], dtype=np.float64)
+    return out.reshape(np.shape(codes))
+
+
 def deq(w, dtype, cols):
-    """Whole [rows, cols] weight matrix widened to float64 (row by row)."""
+    """Whole [rows, cols] weight matrix widened to float64 (row by row).  An
+    fp8 matrix is the flat buffer of its codes followed by its row scales."""
     lib = _load()
     w = _c(w)
-    rows = w.shape[0]
+    rows = w.size // (cols + 4) if dtype == "fp8" else w.shape[0]
     out = np.empty((rows, cols), dtype=np.float64)
     for i in range(rows):
-        _rc(lib.oracle_deq_row(_p(w), _DT[dtype], cols, i, _p(out[i])), "deq_row")
+        _rc(lib.oracle_deq_row(_p(w), _DT[dtype], rows, cols, i, _p(out[i])), "deq_row")
     return out
 
 

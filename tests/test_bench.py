@@ -97,3 +97,12 @@ def test_cpu_baseline_pins_one_core_and_restores_affinity():
     assert out["value"] > 0 and out["dense_tokens_per_s"] > 0
     assert isinstance(out["cpu_model"], str) and out["cpu_model"]
     assert "16 steps" in out["sample"] and "2 of 2 layers" in out["sample"]
+
+
+def test_fp8_predictor_bytes_by_hand():
+    # fp8 predictor: one byte per weight plus a 4-byte scale per row
+    L = _layer(p_dtype="fp8")
+    pred = (4 * 8 + 32 * 4) * 1 + (4 + 4) * (4 + 32)
+    assert bench.step_bytes([L], [5], 2) == pred + 280 + 32 + 160
+    assert bench.dominant_kernel_bytes(L, 5, 1) == \
+        32 * (4 + 4 + 4 + 1) + 5 * (3 * 16 + 4 + 8) + (4 + 8) * 4

@@ -52,6 +52,69 @@ def test_f16_decode_all_bit_patterns():
     assert math.copysign(1.0, ours[0x8000]) == -1.0
 
 
+def test_e4m3_decode_all_codes():
+    """Every OCP E4M3 code against torch's float8_e4m3fn widening (a library
+    the oracle does not use), and hand values from the format's definition:
+    1.0 = 0x38 (exponent 7 = bias), the largest finite 448 = 0x7E, the
+    smallest normal 2^-6 = 0x08, the smallest subnormal 2^-9 = 0x01, signed
+    zero, and the two NaN codes (no infinities)."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9 and ours[0x07] == 7 * 2.0 ** -9
+    assert ours[0x39] == 1.125 and ours[0x40] == 2.0 and ours[0xC0] == -2.0
+    assert ours[0] == 0.0 and math.copysign(1.0, ours[0x80]) == -1.0
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+
+
+def _fp8_buffer(codes, scales):
+    return np.concatenate([np.ascontiguousarray(codes, np.uint8).ravel(),
+                           np.asarray(scales, np.float32).view(np.uint8)])
+
+
+def test_fp8_rows_scale_per_row():
+    """A matrix of fp8 codes with one fp32 scale per row: weight (i, k) =
+    e4m3(code) * scale_i, exactly (compared in binary64 with torch's decode)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    rows, cols = 5, 48
+    codes = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A  # no NaN codes
+    scales = np.float32([0.5, 3e-3, 1.0, 7.25, 1e-5])
+    got = oracle.deq(_fp8_buffer(codes, scales), "fp8", cols)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, vals * scales.astype(np.float64)[:, None])
+
+
+def test_fp8_predictor_equals_its_exact_values():
+    """A predictor stored as fp8 rows with power-of-two row scales (so every
+    weight is exactly a binary32 value) gives bit for bit the logits and mask
+    of the same predictor stored as fp32."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    d, F, r = 32, 40, 16
+    L = _rand_layer(rng, "relu", d, F, r=r)
+    c1 = rng.integers(0, 0x7F, (r, d), dtype=np.uint8) | (rng.integers(0, 2, (r, d)) << 7)
+    c2 = rng.integers(0, 0x7F, (F, r), dtype=np.uint8) | (rng.integers(0, 2, (F, r)) << 7)
+    c1, c2 = c1.astype(np.uint8), c2.astype(np.uint8)
+    s1 = np.float32(2.0) ** rng.integers(-12, -6, r)
+    s2 = np.float32(2.0) ** rng.integers(-10, -4, F)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()  # noqa
+    L32 = dict(L, p_w1=(dec(c1) * s1[:, None]).astype(np.float32),
+               p_w2=(dec(c2) * s2[:, None]).astype(np.float32))
+    L8 = dict(L, p_dtype="fp8", p_w1=_fp8_buffer(c1, s1), p_w2=_fp8_buffer(c2, s2))
+    assert np.array_equal(oracle.deq(L8["p_w1"], "fp8", d), L32["p_w1"].astype(np.float64))
+    x = rng.standard_normal(d)
+    h32, l32, m32 = oracle.predict(L32, x)
+    h8, l8, m8 = oracle.predict(L8, x)
+    assert np.array_equal(h8, h32) and np.array_equal(l8, l32) and np.array_equal(m8, m32)
+
+
 def test_q4_0_block_hand_values():
     """One block with scale 0.5 (fp16 0x3800): code k in the low nibble of
     byte k, code k+16 in the high nibble; value (code - 8) * scale."""

@@ -125,3 +125,31 @@ def test_stack_keeps_configured_activity_at_depth():
             act[l] += o["union"].mean() / 24
             h = o["h"]
     assert np.all(np.abs(act - cfg.mean_activity) < 0.015), act
+
+
+def test_fp8_predictor_layer():
+    """An fp8 predictor is stored as E4M3 codes plus one scale per row, the
+    scale maps each row's largest weight to 448, and the predictor still
+    realises the configured density on fresh tokens (the shift is fitted on
+    the decoded weights)."""
+    from dataclasses import replace
+
+    from workloads import fp8_pack
+    cfg = replace(TINY, p_dtype="fp8")
+    w = make_layer(cfg, 0, seed=0, n_cal=2048)
+    r, d, F = cfg.r, cfg.d, cfg.d_ffn
+    assert w["p_w1"].dtype == torch.uint8 and w["p_w1"].numel() == r * (d + 4)
+    assert w["p_w2"].numel() == F * (r + 4)
+    L = layer_to_numpy(w)
+    W1 = oracle.deq(L["p_w1"], "fp8", d)
+    scales = L["p_w1"][r * d:].view(np.float32)
+    assert np.array_equal(np.abs(W1).max(axis=1), 448.0 * scales.astype(np.float64))
+    # the values the generator works with are the codes times the scales
+    buf, vals = fp8_pack(torch.from_numpy(W1.astype(np.float32)))
+    codes = buf[:r * d].numpy().reshape(r, d)
+    sc = buf[r * d:].numpy().view(np.float32)
+    assert np.array_equal(vals.numpy(), (oracle.e4m3_to_f64(codes) * sc[:, None]).astype(np.float32))
+    L["t"] = oracle.logit_threshold(L["tau"])
+    X = make_tokens(d, 64, 1, seed=5)[:, 0, :].double().numpy()
+    dens = np.mean([oracle.predict(L, x)[2].mean() for x in X])
+    assert abs(dens - cfg.mean_activity) < 0.03, dens

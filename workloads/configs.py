@@ -20,7 +20,7 @@ class Config:
     d_ffn: int
     layers: int
     w_dtype: str         # "f32" | "f16" | "q4_0"
-    p_dtype: str         # predictor weights: "f32" | "f16"
+    p_dtype: str         # predictor weights: "f32" | "f16" | "fp8" (E4M3, a scale per row)
     r: int               # predictor hidden width
     gamma: float         # power-law exponent of firing probability vs rank
     mean_activity: float
@@ -54,9 +54,19 @@ LLAMA2_70B = Config(
     hot_first=True,
     description="Llama2-70B-shaped ReGLU FFN, fp16, hot-first permuted rows")
 
+# The same stack with an 8-bit predictor (OCP E4M3 codes, one fp32 scale per
+# row): half the predictor bytes ([x64] list item 2 and [Guide] section 3
+# describe a small, low-rank predictor; its bytes are a third of a step here).
+LLAMA2_70B_FP8P = Config(
+    name="llama2_70b_reglu_fp8pred", kind="reglu", d=8192, d_ffn=28672, layers=80, w_dtype="f16",
+    p_dtype="fp8", r=1024, gamma=1.2, mean_activity=0.10, tokens=256, batches=(1, 4, 16),
+    hot_first=True,
+    description="Llama2-70B-shaped ReGLU FFN, fp16, hot-first rows, fp8 (E4M3) predictor")
+
 OPT_175B_Q4 = Config(
     name="opt_175b_relu_q4_0", kind="relu", d=12288, d_ffn=49152, layers=96, w_dtype="q4_0",
     p_dtype="f16", r=1024, gamma=1.3, mean_activity=0.05, tokens=128,
     description="OPT-175B-shaped ReLU FFN with 4-bit (Q4_0 block) weights, fp16 predictor")
 
-ALL = {c.name: c for c in (TINY, LLAMA2_7B, FALCON_40B, LLAMA2_70B, OPT_175B_Q4)}
+ALL = {c.name: c for c in (TINY, LLAMA2_7B, FALCON_40B, LLAMA2_70B, LLAMA2_70B_FP8P,
+                           OPT_175B_Q4)}

@@ -80,6 +80,34 @@ def q4_0_values(codes, scales):
     return (codes.float() - 8.0) * s
 
 
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_pack(w):
+    """Predictor weights w fp32 [rows, cols] as OCP E4M3 codes with one fp32
+    scale per row (max |w_i| / 448, so the largest weight of a row maps to the
+    largest finite code), rounded to nearest even.  Returns (uint8 buffer of
+    the rows*cols codes followed by the rows' fp32 scales, the fp32 values
+    code * scale the buffer stands for)."""
+    amax = w.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / FP8_E4M3_MAX, torch.ones_like(amax)).float()
+    q = (w / scale[:, None]).clamp(-FP8_E4M3_MAX, FP8_E4M3_MAX).cpu().to(torch.float8_e4m3fn)
+    codes = q.view(torch.uint8).to(w.device)
+    vals = q.to(torch.float32).to(w.device) * scale[:, None]
+    buf = torch.cat([codes.reshape(-1), scale.contiguous().view(torch.uint8)])
+    return buf, vals
+
+
+def _pred_store(w, p_dtype):
+    """(stored tensor, fp32 values) of one predictor matrix."""
+    if p_dtype == "fp8":
+        return fp8_pack(w)
+    if p_dtype == "f16":
+        w = w.half()
+        return w, w.float()
+    return w, w
+
+
 def _weights(cfg, g_codes_or_normal, g_scales, shape, device):
     """(stored tensor, fp32 values) of one weight matrix."""
     rows, cols = shape
@@ -148,9 +176,8 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
         del zd
 
     # predictor first layer
-    w1 = torch.randn(r, d, generator=_gen(dev, seed, layer, TAG_W1), device=dev) * d ** -0.5
-    if cfg.p_dtype == "f16":
-        w1 = w1.half()
+    w1, w1v = _pred_store(torch.randn(r, d, generator=_gen(dev, seed, layer, TAG_W1), device=dev)
+                          * d ** -0.5, cfg.p_dtype)
     b1 = torch.zeros(r, device=dev)
 
     # second layer fitted on calibration tokens
@@ -158,7 +185,7 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
         xc = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_CAL), device=dev)
     else:
         xc = cal_inputs[0]
-    hcal = torch.relu(xc @ w1.float().t() + b1)
+    hcal = torch.relu(xc @ w1v.t() + b1)
     zcal = (xc @ act_vals.t() if zfit is None else zfit) + b_act
     del xc, zfit
     ha = torch.cat([hcal, torch.ones(n_cal, 1, device=dev)], dim=1).double()
@@ -168,10 +195,8 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
     Ainv = torch.from_numpy(np.linalg.inv(A.cpu().numpy())).to(dev)
     sol = Ainv @ (ha.t() @ zcal.double())          # [r+1, F]
     del zcal
-    w2 = sol[:r].t().float().contiguous()
+    w2, w2v = _pred_store(sol[:r].t().float().contiguous(), cfg.p_dtype)
     b2 = sol[r].float()
-    if cfg.p_dtype == "f16":
-        w2 = w2.half()
     # the per-neuron shift is taken on held-out tokens: the fit's own tokens have
     # less residual variance than new ones, which would bias every rate upward
     del hcal
@@ -179,9 +204,9 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
         xq = torch.randn(n_cal, d, generator=_gen(dev, seed, layer, TAG_SHIFT), device=dev)
     else:
         xq = cal_inputs[1]
-    hq = torch.relu(xq @ w1.float().t() + b1)
+    hq = torch.relu(xq @ w1v.t() + b1)
     del xq
-    lcal = hq @ w2.float().t() + b2                  # [n_cal, F]
+    lcal = hq @ w2v.t() + b2                         # [n_cal, F]
     del hq
     srt = torch.sort(lcal, dim=0, descending=True).values
     del lcal
@@ -203,6 +228,8 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
         out["act_values"] = act_vals
         out["up_values"] = up_vals
         out["down_values"] = down_vals
+        out["p_w1_values"] = w1v
+        out["p_w2_values"] = w2v
     return out
 
 
@@ -219,8 +246,8 @@ def _carry(w, n):
     del z
     if w["kind"] == "reglu":
         a = a * (n @ w["up_values"].t())
-    hid = torch.relu(n @ w["p_w1"].float().t() + w["p_b1"])
-    logit = hid @ w["p_w2"].float().t() + w["p_b2"]
+    hid = torch.relu(n @ w["p_w1_values"].t() + w["p_b1"])
+    logit = hid @ w["p_w2_values"].t() + w["p_b2"]
     del hid
     t = math.log(w["tau"] / (1.0 - w["tau"]))
     a = torch.where(logit > t, a, torch.zeros((), device=a.device))
@@ -247,7 +274,7 @@ def make_stack(cfg: Config, seed: int = 0, device="cpu", n_cal: int = 4096, n_la
             for h, n in zip(hs, ns):
                 h += _carry(w, n)
         del ns
-        for k in ("act_values", "up_values", "down_values"):
+        for k in ("act_values", "up_values", "down_values", "p_w1_values", "p_w2_values"):
             w.pop(k)
         yield w
 
