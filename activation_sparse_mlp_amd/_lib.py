@@ -32,7 +32,7 @@ class SpffnError(RuntimeError):
 class LayerDesc(C.Structure):
     _fields_ = [("d", C.c_int32), ("d_ffn", C.c_int32), ("r", C.c_int32),
                 ("kind", C.c_int32), ("w_dtype", C.c_int32), ("p_dtype", C.c_int32),
-                ("tau", C.c_float), ("reserved", C.c_int32),
+                ("tau", C.c_float), ("dense_prefix", C.c_int32),
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down_t", C.c_void_p),
                 ("b_act", C.c_void_p), ("p_w1", C.c_void_p), ("p_b1", C.c_void_p),
                 ("p_w2", C.c_void_p), ("p_b2", C.c_void_p)]
@@ -189,6 +189,7 @@ class Layer:
         self.kind, self.w_dtype, self.p_dtype = w["kind"], w["w_dtype"], w["p_dtype"]
         self.d, self.d_ffn, self.r = int(w["d"]), int(w["d_ffn"]), int(w["r"])
         self.tau = float(w["tau"])
+        self.dense_prefix = int(w.get("dense_prefix", 0) or 0)
         wd = {"f32": torch.float32, "f16": torch.float16, "q4_0": torch.uint8}[self.w_dtype]
         pd = {"f32": torch.float32, "f16": torch.float16, "fp8": torch.uint8}[self.p_dtype]
         if min(self.d, self.d_ffn, self.r) <= 0:
@@ -220,7 +221,7 @@ class Layer:
         self.tensors = t
         desc = LayerDesc(d=self.d, d_ffn=self.d_ffn, r=self.r, kind=_KINDS[self.kind],
                          w_dtype=_DTYPES[self.w_dtype], p_dtype=_DTYPES[self.p_dtype],
-                         tau=self.tau, reserved=0,
+                         tau=self.tau, dense_prefix=self.dense_prefix,
                          w_gate=_ptr(t.get("w_gate")), w_up=_ptr(t["w_up"]),
                          w_down_t=_ptr(t["w_down_t"]), b_act=_ptr(t["b_act"]),
                          p_w1=_ptr(t["p_w1"]), p_b1=_ptr(t["p_b1"]), p_w2=_ptr(t["p_w2"]),
@@ -587,16 +588,22 @@ def stream_read(buf, sink=None):
 PERMUTED_KEYS = ("w_gate", "w_up", "w_down_t", "b_act", "p_w2", "p_b2")
 
 
-def hot_first_permute(w, calib_x):
+def hot_first_permute(w, calib_x, dense_prefix=False):
     """Load-time hot-first ordering of one layer dict (device tensors): profile
     the activated projection on calib_x [N, d], order neurons by descending
     count (ties by index), and permute every per-neuron row.  Returns
     (permuted dict, perm int32 [d_ffn], counts int32 [d_ffn]); stored neuron k
-    of the result is neuron perm[k] of `w`."""
-    layer = Layer(w)
+    of the result is neuron perm[k] of `w`.
+
+    dense_prefix: also mark the neurons that fired on every calibration token
+    (the leading ones after the order) as the layer's always-active prefix."""
+    layer = Layer(dict(w, dense_prefix=0))
     counts = profile(layer, calib_x)
     perm = hot_first_order(counts)
     out = dict(w)
+    if dense_prefix:
+        N = calib_x.shape[0] if calib_x.dim() == 2 else 1
+        out["dense_prefix"] = int((counts == N).sum())  # one synchronisation, at load
     F = int(w["d_ffn"])
     for k in PERMUTED_KEYS:
         if w.get(k) is not None and (k != "w_gate" or w["kind"] == "reglu"):

@@ -221,8 +221,8 @@ spffn_status run_predict(const Layer &L, const float *x, int B, bool normalize, 
     }
     SPFFN_HIP(launch_gemv_hid(D.p_dtype, L.w1, D.r, D.d, xin, B, D.p_b1, w.hid, s),
               "predictor layer-1 launch");
-    SPFFN_HIP(launch_gemv_mask(D.p_dtype, L.w2, D.d_ffn, D.r, w.hid, B, D.p_b2, L.t, tvec, logits,
-                               mask, uni, s),
+    SPFFN_HIP(launch_gemv_mask(D.p_dtype, L.w2, D.d_ffn, D.r, w.hid, B, D.p_b2, L.t, tvec,
+                               D.dense_prefix, logits, mask, uni, s),
               "predictor layer-2 launch");
     return SPFFN_OK;
 }
@@ -332,7 +332,7 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
         Ws w = carve(L, 1, ws);
         if (trace && trace->h_in)
             SPFFN_HIP(launch_copy_words(h, trace->h_in + l * (size_t)d, d, s), "trace copy launch");
-        SPFFN_HIP(launch_w1_b1(L, h, model->eps, true, w.hid, w.scale, s),
+        SPFFN_HIP(launch_w1_b1(L, h, model->eps, true, w.hid, w.scale, s, tvec ? tvec + l : nullptr),
                   "predictor layer-1 launch");
         float *lg = (trace && trace->logits) ? trace->logits + logit_off : nullptr;
         hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -343,8 +343,7 @@ spffn_status decode_one_token(const spffn_model *model, const float *x, float *h
         const int chunks = fused_chunks(L);
         int32_t *lc = layer_counts ? layer_counts + l : nullptr;
         SPFFN_HIP(launch_layer_b1(L, w.hid, h, w.scale, lg, w.uni, w.lst_i, w.lst_a, w.done, w.part,
-                                  lc ? w.gcnt : nullptr, w.status, tvec ? tvec + l : nullptr, s,
-                                  e0, e1),
+                                  lc ? w.gcnt : nullptr, w.status, tvec != nullptr, s, e0, e1),
                   "predictor layer-2 + gather + down launch");
         if (trace && trace->union_mask)
             SPFFN_HIP(hipMemcpyAsync(trace->union_mask + mask_off, w.uni, F, hipMemcpyDeviceToDevice,
@@ -405,7 +404,9 @@ spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out)
                     elems_multiple(D.p_dtype));
     if (!(D.tau > 0.0f && D.tau < 1.0f))
         return fail(SPFFN_E_ARG, "layer_create: tau=%g outside (0, 1)", (double)D.tau);
-    if (D.reserved != 0) return fail(SPFFN_E_ARG, "layer_create: reserved must be 0");
+    if (D.dense_prefix < 0 || D.dense_prefix > D.d_ffn)
+        return fail(SPFFN_E_SHAPE, "layer_create: dense_prefix=%d outside [0, d_ffn=%d]",
+                    D.dense_prefix, D.d_ffn);
     if (!D.w_up || !D.w_down_t || !D.p_w1 || !D.p_b1 || !D.p_w2 || !D.p_b2)
         return fail(SPFFN_E_ARG, "layer_create: a required weight pointer is NULL");
     if (D.kind == SPFFN_REGLU && !D.w_gate)

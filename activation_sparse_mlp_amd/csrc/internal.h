@@ -65,9 +65,10 @@ hipError_t launch_q4_0_repack(const void *aos, void *soa, int rows, int cols, hi
 hipError_t launch_gemv_hid(int fmt, WMat w, int rows, int cols, const float *x, int B,
                            const float *bias, float *out, hipStream_t s);
 // tvec (or nullptr): per-token thresholds [B] replacing t
+// kd: rows [0, kd) always active (an always-active prefix)
 hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x, int B,
-                            const float *bias, float t, const float *tvec, float *logits,
-                            uint8_t *mask, uint8_t *uni, hipStream_t s);
+                            const float *bias, float t, const float *tvec, int kd,
+                            float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s);
 hipError_t launch_gemv_count(int fmt, WMat w, int rows, int cols, const float *x, int B,
                              const float *bias, int32_t *counts, hipStream_t s);
 
@@ -91,8 +92,10 @@ hipError_t launch_rms_scale(const float *h, int B, int d, float eps, float *scal
 // Single-token kernels (kernels_b1.hip); usable when b1_fits(L).
 bool b1_fits(const Layer &L);
 int down_b1_chunks(const Layer &L);
+// scale_out (or nullptr): [0] the RMS scale, [1] the logit threshold (tvec[0]
+// when tvec is given, else the layer's) for the single-token layer kernel
 hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
-                        float *scale_out, hipStream_t s);
+                        float *scale_out, hipStream_t s, const float *tvec = nullptr);
 hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t *mask,
                         const float *tvec, hipStream_t s);
 hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, const int32_t *idx,
@@ -145,7 +148,9 @@ int fused_chunks(const Layer &L);
 int fused_per_chunk(const Layer &L);
 size_t fused_list_slots(const Layer &L);  // list slots of the layer kernel (RB per row group)
 // Predictor layer 2 + threshold + gate/up gather + down projection of one
-// layer (single token) in one launch.  done holds fused_chunks(L) counters,
+// layer (single token) in one launch.  `scale` holds the RMS scale and the
+// token's logit threshold, as launch_w1_b1 writes them; the threshold is read
+// from there only with `adapt` (else the layer's own is used).  done holds fused_chunks(L) counters,
 // kFusedDoneStride words apart, which must be zero (the whole region may be
 // cleared).
 constexpr int kFusedDoneStride = 1024;
@@ -158,7 +163,7 @@ void set_chunk_wait_polls(int polls);
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
                            int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
-                           const float *tvec, hipStream_t s, hipEvent_t ev_start = nullptr,
+                           bool adapt, hipStream_t s, hipEvent_t ev_start = nullptr,
                            hipEvent_t ev_stop = nullptr);
 
 }  // namespace spffn

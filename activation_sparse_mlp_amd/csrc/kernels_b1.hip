@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void w1_b1_kernel(WMat w1, int r, int d,
                                                     const float *__restrict__ h, float eps,
                                                     int normalize, const float *__restrict__ b1,
                                                     float *__restrict__ hid,
-                                                    float *__restrict__ scale_out) {
+                                                    float *__restrict__ scale_out,
+                                                    const float *__restrict__ tvec, float t) {
     constexpr int E = PacketElems<PF>::value;
     constexpr int U = 16;
     extern __shared__ float xl[];
@@ -103,7 +104,12 @@ __global__ __launch_bounds__(256) void w1_b1_kernel(WMat w1, int r, int d,
     }
     const float ss = block_sum(stage_vec<E>(h, d, xl), red);  // contains the barrier
     const float s = normalize ? 1.0f / sqrtf(ss / (float)d + eps) : 1.0f;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
+    // scale_out[0] = the RMS scale, scale_out[1] = the token's logit
+    // threshold (its own, or the layer's): the layer kernel reads both at once
+    if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) {
+        scale_out[0] = s;
+        scale_out[1] = tvec ? *tvec : t;
+    }
 
     float acc[1] = {0.0f};
     for (int pg = 0; pg < NP; pg += 64 * U) {
@@ -131,7 +137,7 @@ template <int PF, int R>
 __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
                                                     const float *__restrict__ hid,
                                                     const float *__restrict__ b2, float t,
-                                                    const float *__restrict__ tvec,
+                                                    const float *__restrict__ tvec, int kd,
                                                     float *__restrict__ logits,
                                                     uint8_t *__restrict__ mask) {
     constexpr int E = PacketElems<PF>::value;
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
 #pragma unroll
         for (int u = 0; u < PL; ++u) {
             const int p = u * 64 + lane;
-            raw[q][u] = (row0 + q < rows && p < NP)
+            raw[q][u] = (row0 + q < rows && row0 + q >= kd && p < NP)
                             ? ld_stream(row_ptr<PF>(w2, row0 + q, r) + p)
                             : make_uint4(0, 0, 0, 0);
         }
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
 #pragma unroll
                 for (int u = 0; u < PL; ++u) {
                     const int p = pg + u * 64 + lane;
-                    raw[q][u] = (row0 + q < rows && p < NP)
+                    raw[q][u] = (row0 + q < rows && row0 + q >= kd && p < NP)
                                     ? ld_stream(row_ptr<PF>(w2, row0 + q, r) + p)
                                     : make_uint4(0, 0, 0, 0);
                 }
@@ -182,9 +188,10 @@ __global__ __launch_bounds__(256) void w2_b1_kernel(WMat w2, int rows, int r,
         const int row = row0 + q;
         const float v = wave_sum(acc[q][0]) * row_scale<PF>(w2, row < rows ? row : 0);
         if (lane == 0 && row < rows) {
-            const float l = v + b2[row];
+            const bool pre = row < kd;  // always-active prefix
+            const float l = pre ? __builtin_inff() : v + b2[row];
             if (logits) logits[row] = l;
-            mask[row] = (uint8_t)(l > (tvec ? tvec[0] : t));
+            mask[row] = (uint8_t)(pre || l > (tvec ? tvec[0] : t));
         }
     }
 }
@@ -441,7 +448,7 @@ struct FusedArgs {
     const float *hid;     // [r]
     const float *b2;      // [d_ffn]
     float t;
-    const float *tvec;    // the token's threshold (device, replaces t), or nullptr
+    int kd;               // always-active prefix: rows [0, kd) are not scored
     const float *bias;    // [d_ffn] or nullptr
     const float *h;       // [d] residual stream (un-normalised)
     const float *scale;   // device RMS scale
@@ -451,9 +458,10 @@ struct FusedArgs {
     float *lst_a;         // [G*RB]
     int per_chunk;        // NG: consecutive groups per down-projection chunk
     int32_t *done;        // [C * kDoneStride] groups published per chunk (zero at launch)
+    bool adapt;           // host only: the token's threshold is at scale[1], not t
 };
 
-template <int PF, int FMT, bool GATED, int RW, int UA>
+template <int PF, int FMT, bool GATED, int RW, int UA, bool ADAPT>
 __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
@@ -471,11 +479,14 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     // lane's two packets, the rows' b2 entries (lane q holds row q's) and the
     // bias of each of the group's rows (into LDS).  Addresses are clamped into
     // range and out-of-range values discarded, so the loads carry no branches.
+    // Rows of the always-active prefix are not scored: their loads are
+    // redirected to one fixed row (the last), so that no W2 row of the prefix
+    // is read from memory while every load stays unconditional.
     uint4 rc[RW][PL];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
         const int row = g + G * (wv + 4 * q);
-        const bool rv = row < a.d_ffn;
+        const bool rv = row < a.d_ffn && row >= a.kd;
         const int rr = rv ? row : a.d_ffn - 1;
 #pragma unroll
         for (int u = 0; u < PL; ++u) {
@@ -502,8 +513,19 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         const int row = g + G * (int)threadIdx.x;
         s_bias[threadIdx.x] = (a.bias && row < a.d_ffn) ? a.bias[row] : 0.0f;
     }
-    const float s = *a.scale;
-    const float thr = a.tvec ? *a.tvec : a.t;
+    // The RMS scale, and the threshold: the layer's, a kernel argument, or
+    // (ADAPT, a threshold per token) the one predictor layer 1 wrote beside
+    // the scale.  The plain step keeps the argument: a mask that waits on a
+    // loaded threshold costs about 1 us per launch.
+    float s, thr;
+    if constexpr (ADAPT) {
+        const float2 st = *reinterpret_cast<const float2 *>(a.scale);
+        s = st.x;
+        thr = st.y;
+    } else {
+        s = *a.scale;
+        thr = a.t;
+    }
 
     // logits, threshold, mask
     uint32_t bits = 0;
@@ -518,8 +540,9 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v), q));
         const int row = g + G * (wv + 4 * q);
         if (row < a.d_ffn) {
-            const float l = v + bq;
-            const bool m = l > thr;
+            const bool pre = row < a.kd;  // always-active prefix
+            const float l = pre ? __builtin_inff() : v + bq;
+            const bool m = pre || l > thr;
             bits |= (uint32_t)m << q;
             if (lane == 0) {
                 if (a.logits) a.logits[row] = l;
@@ -805,11 +828,11 @@ constexpr int layer_b1_waves() {
     return (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
 }
 
-template <int PF, int FMT, bool GATED, int RW, int UA, int UR>
+template <int PF, int FMT, bool GATED, int RW, int UA, int UR, bool ADAPT>
 __global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer_b1_kernel(
     FusedArgs f, DownListArgs dn, int slices) {
     if ((int)blockIdx.x < f.groups) {
-        fused_group<PF, FMT, GATED, RW, UA>(f, blockIdx.x);
+        fused_group<PF, FMT, GATED, RW, UA, ADAPT>(f, blockIdx.x);
         return;
     }
     const int q = (int)blockIdx.x - f.groups;
@@ -846,19 +869,19 @@ bool b1_fits(const Layer &L) {
 }
 
 hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
-                        float *scale_out, hipStream_t s) {
+                        float *scale_out, hipStream_t s, const float *tvec) {
     const spffn_layer_desc &D = L.desc;
     const int blocks = (D.r + 3) / 4;
     const size_t lds = (size_t)D.d * 4;
     if (D.p_dtype == SPFFN_F16)
         w1_b1_kernel<kF16><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out);
+                                                    scale_out, tvec, L.t);
     else if (D.p_dtype == SPFFN_FP8_E4M3)
         w1_b1_kernel<kFP8><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out);
+                                                    scale_out, tvec, L.t);
     else
         w1_b1_kernel<kF32><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out);
+                                                    scale_out, tvec, L.t);
     return hipGetLastError();
 }
 
@@ -870,13 +893,13 @@ hipError_t launch_w2_b1(const Layer &L, const float *hid, float *logits, uint8_t
     const size_t lds = (size_t)D.r * 4;
     if (D.p_dtype == SPFFN_F16)
         w2_b1_kernel<kF16, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
-                                                       logits, mask);
+                                                       D.dense_prefix, logits, mask);
     else if (D.p_dtype == SPFFN_FP8_E4M3)
         w2_b1_kernel<kFP8, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
-                                                       logits, mask);
+                                                       D.dense_prefix, logits, mask);
     else
         w2_b1_kernel<kF32, R><<<blocks, 256, lds, s>>>(L.w2, D.d_ffn, D.r, hid, D.p_b2, L.t, tvec,
-                                                       logits, mask);
+                                                       D.dense_prefix, logits, mask);
     return hipGetLastError();
 }
 
@@ -1027,26 +1050,33 @@ bool fused_fits(const Layer &L) {
            L.desc.d / packet_elems(L.desc.w_dtype) <= 256 * 8;
 }
 
-template <int PF, int FMT, bool GATED, int RW, int UA>
+template <int PF, int FMT, bool GATED, int RW, int UA, bool ADAPT>
 static void launch_layer_t(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
                            hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int UR = FMT == kQ4 ? 8 : 16;
     // with timing events the dispatch itself is timestamped (the events bracket
     // the kernel's execution, not its launch)
     if (e0 || e1)
-        hipExtLaunchKernelGGL(layer_b1_kernel<PF, FMT, GATED, RW, UA, UR>, dim3(blocks), dim3(256), 0,
+        hipExtLaunchKernelGGL(layer_b1_kernel<PF, FMT, GATED, RW, UA, UR, ADAPT>, dim3(blocks),
+                              dim3(256), 0,
                               s, e0, e1, 0, f, dn, slices);
     else
-        layer_b1_kernel<PF, FMT, GATED, RW, UA, UR><<<blocks, 256, 0, s>>>(f, dn, slices);
+        layer_b1_kernel<PF, FMT, GATED, RW, UA, UR, ADAPT><<<blocks, 256, 0, s>>>(f, dn, slices);
 }
 
 template <int PF, int FMT, bool GATED>
 static void launch_layer_rw(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
                             int UA, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int RW = fused_rw<FMT, GATED>();
-    if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2>(f, dn, slices, blocks, s, e0, e1);
-    else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4>(f, dn, slices, blocks, s, e0, e1);
-    else launch_layer_t<PF, FMT, GATED, RW, 8>(f, dn, slices, blocks, s, e0, e1);
+    if (f.adapt) {
+        if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2, true>(f, dn, slices, blocks, s, e0, e1);
+        else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4, true>(f, dn, slices, blocks, s, e0, e1);
+        else launch_layer_t<PF, FMT, GATED, RW, 8, true>(f, dn, slices, blocks, s, e0, e1);
+    } else {
+        if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2, false>(f, dn, slices, blocks, s, e0, e1);
+        else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4, false>(f, dn, slices, blocks, s, e0, e1);
+        else launch_layer_t<PF, FMT, GATED, RW, 8, false>(f, dn, slices, blocks, s, e0, e1);
+    }
 }
 
 template <int PF, int FMT>
@@ -1059,8 +1089,7 @@ static void launch_layer_kind(const FusedArgs &f, const DownListArgs &dn, bool g
 hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, const float *scale,
                            float *logits, uint8_t *mask, int32_t *lst_i, float *lst_a,
                            int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
-                           const float *tvec, hipStream_t s, hipEvent_t ev_start,
-                           hipEvent_t ev_stop) {
+                           bool adapt, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
     const bool gated = D.kind == SPFFN_REGLU;
     const int G = fused_groups(L), UA = fused_ua(L), C = fused_chunks(L), NG = fused_per_chunk(L);
@@ -1076,7 +1105,8 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     f.hid = hid;
     f.b2 = D.p_b2;
     f.t = L.t;
-    f.tvec = tvec;
+    f.kd = D.dense_prefix;
+    f.adapt = adapt;
     f.bias = D.b_act;
     f.h = h;
     f.scale = scale;

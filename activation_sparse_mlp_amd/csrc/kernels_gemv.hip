@@ -20,6 +20,7 @@ struct GemvArgs {
     const float *bias;  // [rows] or nullptr
     float t;
     const float *tvec;  // kEpiMask: per-token thresholds [B] replacing t, or nullptr
+    int kd;             // kEpiMask: rows [0, kd) always active (logit reported +inf)
     float *out;         // kEpiHid: [B, rows]
     float *logits;      // kEpiMask: [B, rows] or nullptr
     uint8_t *mask;      // kEpiMask: [B, rows] or nullptr
@@ -42,8 +43,9 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, const 
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b < a.B) {
-                const float l = v[b] + bias;
-                const uint8_t m = (uint8_t)(l > (a.tvec ? a.tvec[b] : a.t));
+                const bool pre = row < a.kd;
+                const float l = pre ? __builtin_inff() : v[b] + bias;
+                const uint8_t m = (uint8_t)(pre || l > (a.tvec ? a.tvec[b] : a.t));
                 if (a.logits) a.logits[(size_t)b * a.rows + row] = l;
                 if (a.mask) a.mask[(size_t)b * a.rows + row] = m;
                 u |= m;
@@ -236,8 +238,8 @@ hipError_t launch_gemv_hid(int fmt, WMat w, int rows, int cols, const float *x, 
 }
 
 hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x, int B,
-                            const float *bias, float t, const float *tvec, float *logits,
-                            uint8_t *mask, uint8_t *uni, hipStream_t s) {
+                            const float *bias, float t, const float *tvec, int kd,
+                            float *logits, uint8_t *mask, uint8_t *uni, hipStream_t s) {
     GemvArgs a{};
     a.w = w;
     a.rows = rows;
@@ -247,6 +249,7 @@ hipError_t launch_gemv_mask(int fmt, WMat w, int rows, int cols, const float *x,
     a.bias = bias;
     a.t = t;
     a.tvec = tvec;
+    a.kd = kd;
     a.logits = logits;
     a.mask = mask;
     a.uni = uni;

@@ -144,6 +144,7 @@ struct BgArgs {
     const float *bias;     // [rows] or nullptr (mask: b2; act: b_act)
     float t;               // mask: logit threshold
     const float *tvec;     // mask: per-token thresholds [B] replacing t, or nullptr
+    int kd;                // mask: rows [0, kd) always active (logit reported +inf)
     float *part;           // partial: [gridDim.y, B, rows]
     float *logits;         // mask: [B, rows] or nullptr
     uint8_t *mask;         // mask: [B, rows] or nullptr
@@ -344,8 +345,9 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
             if constexpr (EPI == kEpiPartial) {
                 a.part[((size_t)blockIdx.y * a.B + n) * a.rows + rr] = za;
             } else if constexpr (EPI == kEpiMask) {
-                const float l = za + (a.bias ? a.bias[rr] : 0.0f);
-                const bool mk = l > (a.tvec ? a.tvec[n] : a.t);
+                const bool pre = rr < a.kd;
+                const float l = pre ? __builtin_inff() : za + (a.bias ? a.bias[rr] : 0.0f);
+                const bool mk = pre || l > (a.tvec ? a.tvec[n] : a.t);
                 if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
                 if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
                 if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
@@ -693,6 +695,7 @@ hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float
     b.bias = D.p_b2;
     b.t = L.t;
     b.tvec = tvec;
+    b.kd = D.dense_prefix;
     b.logits = logits;
     b.mask = mask;
     b.uni = uni;

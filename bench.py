@@ -92,7 +92,8 @@ def step_bytes(layers, counts, B):
         wp, ps = pred_bytes(L)
         row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
         n_mat = 3 if L.kind == "reglu" else 2
-        total += (L.r * L.d + L.d_ffn * L.r) * wp + (4 + ps) * (L.r + L.d_ffn)
+        kd = getattr(L, "dense_prefix", 0)  # always-active rows are not scored
+        total += (L.r * L.d + (L.d_ffn - kd) * L.r) * wp + (4 + ps) * (L.r + L.d_ffn - kd)
         total += int(u) * (n_mat * row + 4 + 4)
         total += L.d_ffn
         total += B * (2 * L.d + L.r) * 4
@@ -110,7 +111,8 @@ def dominant_kernel_bytes(L, u, B):
     wp, ps = pred_bytes(L)
     row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
     n_mat = 3 if L.kind == "reglu" else 2
-    return (L.d_ffn * (L.r * wp + ps + 4 + 1) + int(u) * (n_mat * row + 4 + 8)
+    kd = getattr(L, "dense_prefix", 0)  # always-active rows are not scored
+    return ((L.d_ffn - kd) * (L.r * wp + ps + 4) + L.d_ffn + int(u) * (n_mat * row + 4 + 8)
             + B * (L.r + L.d) * 4)
 
 
@@ -307,7 +309,7 @@ def main():
     # every layer calibrated on the inputs it receives in this stack
     for l, w in enumerate(make_stack(cfg, seed=0, device=dev, n_cal=args.n_cal, n_layers=nl)):
         if cfg.hot_first:
-            w, _, _ = spffn.hot_first_permute(w, calib)
+            w, _, _ = spffn.hot_first_permute(w, calib, dense_prefix=cfg.dense_prefix)
         layers.append(spffn.Layer(w))
         keep.append(w if l < n_keep else None)
         if l % 10 == 0 or l == nl - 1:

@@ -93,6 +93,15 @@ typedef enum {
  *             when sigmoid(logit_i) > tau, evaluated as logit_i > t with
  *             t = ln(tau / (1 - tau)) computed once in binary64 and rounded to
  *             binary32 (sigmoid is increasing)
+ *   dense_prefix  k in [0, d_ffn]: the first k stored neurons are always
+ *             active, for every token, and the predictor does not score them
+ *             (their p_w2 / p_b2 rows are never read; logits reported for
+ *             them are +inf).  After the hot-first order these are the
+ *             neurons that fire on every profiling token, so the hot set runs
+ *             as a plain dense GEMV with no predictor bytes (Guide section 2,
+ *             hot neurons placed where they are always at hand; section 4,
+ *             neurons pre-grouped into blocks: the always-hot block).  0 is
+ *             the plain predictor.
  * FFN weights are w_dtype (F32, F16 or Q4_0 split layout); predictor weights
  * are p_dtype (F32, F16 or FP8_E4M3: the x64 page's list item 2 and the
  * Guide's section 3 describe a small, low-rank predictor; 8-bit weights halve
@@ -106,7 +115,7 @@ typedef struct {
     int32_t w_dtype;  /* spffn_dtype */
     int32_t p_dtype;  /* spffn_dtype */
     float tau;
-    int32_t reserved; /* must be 0 */
+    int32_t dense_prefix; /* always-active leading neurons, 0 for none */
     const void *w_gate;
     const void *w_up;
     const void *w_down_t;

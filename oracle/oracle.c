@@ -136,10 +136,14 @@ static double dot(const double *a, const double *b, int64_t n)
  *   mask_i  = logit_i > t
  * [Guide] compares sigmoid(logit) > tau strictly; sigmoid is increasing, so
  * this equals logit > t with t = ln(tau / (1 - tau)), which the caller passes.
+ * The first dense_prefix neurons are not scored: they are always active
+ * (the always-hot neurons of [Guide] section 2 run without the predictor)
+ * and their logit is reported as +inf.
  * hid may be NULL; logits and mask may be NULL. */
 int oracle_predict(int64_t d, int64_t d_ffn, int64_t r, int p_dtype,
                    const void *W1, const float *b1, const void *W2, const float *b2,
-                   const double *x, double t, double *hid_out, double *logits, uint8_t *mask)
+                   const double *x, double t, int64_t dense_prefix, double *hid_out,
+                   double *logits, uint8_t *mask)
 {
     int64_t j, i;
     double *row = (double *)malloc(sizeof(double) * (size_t)(d > r ? d : r));
@@ -161,12 +165,17 @@ int oracle_predict(int64_t d, int64_t d_ffn, int64_t r, int p_dtype,
             hid_out[j] = hid[j];
     }
     for (i = 0; i < d_ffn; ++i) {
-        oracle_deq_row(W2, p_dtype, d_ffn, r, i, row);
-        double l = dot(row, hid, r) + (double)b2[i];
+        double l;
+        if (i < dense_prefix) {
+            l = INFINITY;
+        } else {
+            oracle_deq_row(W2, p_dtype, d_ffn, r, i, row);
+            l = dot(row, hid, r) + (double)b2[i];
+        }
         if (logits)
             logits[i] = l;
         if (mask)
-            mask[i] = (uint8_t)(l > t);
+            mask[i] = (uint8_t)(i < dense_prefix || l > t);
     }
     free(row);
     free(hid);

@@ -14,6 +14,8 @@ A layer is a plain dict of numpy arrays and ints:
   p_w2      [d_ffn, r],  p_b2 float32 [d_ffn]
   t         logit threshold (float32 value); a neuron is predicted active
             when its logit is > t
+  dense_prefix  optional k: the first k neurons are always active and not
+            scored (logit +inf)
 
 fp16 arrays are numpy float16; 4-bit arrays are uint8 [rows, cols/32*18] in
 the 18-byte block layout described in oracle.c; fp8 (OCP E4M3) matrices are a
@@ -50,7 +52,8 @@ def _load():
         lib.oracle_e4m3_to_f64.restype = dp
         lib.oracle_deq_row.argtypes = [vp, i32, i64, i64, i64, vp]
         lib.oracle_deq_row.restype = i32
-        lib.oracle_predict.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, dp, vp, vp, vp]
+        lib.oracle_predict.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, dp, i64, vp, vp,
+                                       vp]
         lib.oracle_predict.restype = i32
         lib.oracle_threshold.argtypes = [vp, i64, C.c_float, vp]
         lib.oracle_threshold.restype = None
@@ -139,8 +142,9 @@ def predict(layer, x):
     w1, w2 = _c(L["p_w1"]), _c(L["p_w2"])
     b1, b2 = _c(L["p_b1"], np.float32), _c(L["p_b2"], np.float32)
     _rc(lib.oracle_predict(L["d"], L["d_ffn"], L["r"], _DT[L["p_dtype"]], _p(w1), _p(b1),
-                           _p(w2), _p(b2), _p(x), float(L["t"]), _p(hid), _p(logits),
-                           _p(mask)), "predict")
+                           _p(w2), _p(b2), _p(x), float(L["t"]),
+                           int(L.get("dense_prefix", 0) or 0), _p(hid), _p(logits), _p(mask)),
+        "predict")
     return hid, logits, mask
 
 

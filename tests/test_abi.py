@@ -40,7 +40,7 @@ FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
 
 
 def desc(**kw):
-    base = dict(d=256, d_ffn=1024, r=64, kind=1, w_dtype=1, p_dtype=1, tau=0.5, reserved=0,
+    base = dict(d=256, d_ffn=1024, r=64, kind=1, w_dtype=1, p_dtype=1, tau=0.5, dense_prefix=0,
                 w_gate=FAKE, w_up=FAKE, w_down_t=FAKE, b_act=FAKE, p_w1=FAKE, p_b1=FAKE,
                 p_w2=FAKE, p_b2=FAKE)
     base.update(kw)
@@ -70,7 +70,9 @@ def create(**kw):
     ({"tau": 0.0}, E_ARG),
     ({"tau": 1.0}, E_ARG),
     ({"tau": float("nan")}, E_ARG),
-    ({"reserved": 1}, E_ARG),
+    ({"dense_prefix": 1024}, OK),           # every neuron always active
+    ({"dense_prefix": 1025}, E_SHAPE),
+    ({"dense_prefix": -1}, E_SHAPE),
     ({"w_gate": None}, E_ARG),              # ReGLU needs the gate
     ({"w_up": None}, E_ARG),
     ({"p_b2": None}, E_ARG),

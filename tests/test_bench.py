@@ -106,3 +106,13 @@ def test_fp8_predictor_bytes_by_hand():
     assert bench.step_bytes([L], [5], 2) == pred + 280 + 32 + 160
     assert bench.dominant_kernel_bytes(L, 5, 1) == \
         32 * (4 + 4 + 4 + 1) + 5 * (3 * 16 + 4 + 8) + (4 + 8) * 4
+
+
+def test_dense_prefix_bytes_by_hand():
+    # 6 always-active neurons: their W2 rows, b2 entries are not read (mask
+    # bytes still are); the rest as before
+    L = _layer(dense_prefix=6)
+    pred = (4 * 8 + 26 * 4) * 2 + 4 * (4 + 26)
+    assert bench.step_bytes([L], [5], 2) == pred + 280 + 32 + 160
+    assert bench.dominant_kernel_bytes(L, 5, 1) == \
+        26 * (4 * 2 + 4) + 32 + 5 * (3 * 16 + 4 + 8) + (4 + 8) * 4

@@ -34,7 +34,10 @@ def _build(cfg, layers, hot_first, n_cal=4096):
     calib = make_profile_tokens(cfg.d, 256, seed=1, device=DEV) if hot_first else None
     for l, w in enumerate(make_stack(cfg, seed=0, device=DEV, n_cal=n_cal, n_layers=layers)):
         if hot_first:
-            w, perm, counts = spffn.hot_first_permute(w, calib)
+            w, perm, counts = spffn.hot_first_permute(w, calib, dense_prefix=cfg.dense_prefix)
+            if cfg.dense_prefix:
+                # the prefix is every neuron that fired on all profiling tokens
+                assert w["dense_prefix"] == int((counts == 256).sum()) > 0
             if l < 2:
                 c = counts.cpu().numpy()
                 assert np.array_equal(perm.cpu().numpy(), oracle.hot_first_perm(c))
@@ -80,7 +83,9 @@ def _decode_check(cfg, B, layers, hot_first, tokens_checked=None, layers_checked
         for b in check:
             n = oracle.rmsnorm(h_in[l][b], 1e-5)
             _, ref_lg, _ = oracle.predict(L, n)
-            assert np.max(np.abs(lg[l][b] - ref_lg)) < 1e-3
+            fin = np.isfinite(ref_lg)  # the always-active prefix reports +inf on both sides
+            assert np.array_equal(np.isposinf(lg[l][b]), ~fin)
+            assert np.max(np.abs(lg[l][b][fin] - ref_lg[fin])) < 1e-3
             check_mask_agreement(oracle.threshold(lg[l][b], L["t"]), ref_lg, L["t"])
             y_ref = oracle.ffn_masked(L, n, U)
             err = rel_l2(outs[l][b] - h_in[l][b], y_ref)

@@ -52,6 +52,45 @@ def test_f16_decode_all_bit_patterns():
     assert math.copysign(1.0, ours[0x8000]) == -1.0
 
 
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_dense_prefix_hand(kind):
+    """The hand example with an always-active prefix of two neurons
+    (golden/hand_prefix.json): not scored, forced active, computed."""
+    g = load_golden("hand_prefix.json")
+    L, x, _, _ = _hand_layer(kind)
+    L = dict(L, dense_prefix=g["dense_prefix"])
+    _, logits, mask = oracle.predict(L, x)
+    want = np.array([float(v) for v in g["logits"]])
+    assert np.array_equal(logits, want)
+    assert np.array_equal(mask, np.asarray(g["mask"], np.uint8))
+    assert np.array_equal(oracle.ffn_masked(L, x, mask), np.asarray(g[f"y_{kind}"], np.float64))
+
+
+def test_dense_prefix_invariants():
+    """A prefix leaves the other neurons' logits and decisions as they are; a
+    prefix of every neuron gives the dense FFN bit for bit; and since a
+    forced-on neuron that is in fact inactive contributes an exact zero, the
+    prefix joined with the exact mask still gives the dense FFN exactly."""
+    rng = np.random.default_rng(21)
+    L = _rand_layer(rng, "reglu", 16, 40, r=8)
+    x = rng.standard_normal(16)
+    _, l0, m0 = oracle.predict(L, x)
+    for k in (1, 7, 39):
+        _, lk, mk = oracle.predict(dict(L, dense_prefix=k), x)
+        assert np.all(np.isinf(lk[:k])) and np.all(mk[:k] == 1)
+        assert np.array_equal(lk[k:], l0[k:]) and np.array_equal(mk[k:], m0[k:])
+    Lall = dict(L, dense_prefix=40)
+    h = np.atleast_2d(x)
+    out = oracle.decode_layer(Lall, h, 1e-5)
+    n = oracle.rmsnorm(x, 1e-5)
+    assert np.all(out["union"] == 1)
+    assert np.array_equal(out["y"][0], oracle.ffn_dense(L, n)[0])
+    _, _, exact = oracle.preact(L, n)
+    pre = exact.copy()
+    pre[:12] = 1
+    assert np.array_equal(oracle.ffn_masked(L, n, pre), oracle.ffn_dense(L, n)[0])
+
+
 def test_e4m3_decode_all_codes():
     """Every OCP E4M3 code against torch's float8_e4m3fn widening (a library
     the oracle does not use), and hand values from the format's definition:

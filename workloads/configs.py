@@ -30,6 +30,7 @@ class Config:
     q4_scale_std: float = 0.003  # std of the |N(0, s^2)| block scales (q4_0)
     tau: float = 0.5
     hot_first: bool = False
+    dense_prefix: bool = False  # neurons active on every profiling token run unscored
     description: str = field(default="", compare=False)
 
 
@@ -63,10 +64,19 @@ LLAMA2_70B_FP8P = Config(
     hot_first=True,
     description="Llama2-70B-shaped ReGLU FFN, fp16, hot-first rows, fp8 (E4M3) predictor")
 
+# Hot-first rows with the always-active prefix: the neurons that fire on every
+# profiling token are computed for every token without predictor rows
+# ([Guide] section 2: hot neurons always at hand; section 4: neuron blocks).
+LLAMA2_70B_PREFIX = Config(
+    name="llama2_70b_reglu_prefix", kind="reglu", d=8192, d_ffn=28672, layers=80,
+    w_dtype="f16", p_dtype="f16", r=1024, gamma=1.2, mean_activity=0.10, tokens=256,
+    batches=(1, 4, 16), hot_first=True, dense_prefix=True,
+    description="Llama2-70B-shaped ReGLU FFN, fp16, hot-first rows, always-active prefix")
+
 OPT_175B_Q4 = Config(
     name="opt_175b_relu_q4_0", kind="relu", d=12288, d_ffn=49152, layers=96, w_dtype="q4_0",
     p_dtype="f16", r=1024, gamma=1.3, mean_activity=0.05, tokens=128,
     description="OPT-175B-shaped ReLU FFN with 4-bit (Q4_0 block) weights, fp16 predictor")
 
 ALL = {c.name: c for c in (TINY, LLAMA2_7B, FALCON_40B, LLAMA2_70B, LLAMA2_70B_FP8P,
-                           OPT_175B_Q4)}
+                           LLAMA2_70B_PREFIX, OPT_175B_Q4)}
