@@ -15,11 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspffn.so")
 
 F32, F16, Q4_0, FP8_E4M3 = 0, 1, 2, 3
-RELU, REGLU = 0, 1
+RELU, REGLU, SWIGLU = 0, 1, 2
 MAX_BATCH = 16
 DECODE_DENSE = 1
 _DTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "fp8": FP8_E4M3}
-_KINDS = {"relu": RELU, "reglu": REGLU}
+_KINDS = {"relu": RELU, "reglu": REGLU, "swiglu": SWIGLU}
 _STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_WORKSPACE", -5: "E_HIP"}
 
 
@@ -203,16 +203,16 @@ class Layer:
                  "p_w1": self.r * (self.d + ps), "p_b1": self.r,
                  "p_w2": self.d_ffn * (self.r + ps), "p_b2": self.d_ffn}
         for k, n in sizes.items():  # every size before any device check
-            if isinstance(w.get(k), torch.Tensor) and (k != "w_gate" or self.kind == "reglu"):
+            if isinstance(w.get(k), torch.Tensor) and (k != "w_gate" or self.kind != "relu"):
                 _size(w[k], n, k)
         t = {}
         for k in ("w_gate", "w_up", "w_down_t"):
-            if w.get(k) is not None and (k != "w_gate" or self.kind == "reglu"):
+            if w.get(k) is not None and (k != "w_gate" or self.kind != "relu"):
                 t[k] = _dev(w[k], wd, k, n_w)
                 if self.w_dtype == "q4_0":
                     t[k] = q4_0_repack(t[k], self.d_ffn, self.d)
-        if "w_up" not in t or "w_down_t" not in t or (self.kind == "reglu" and "w_gate" not in t):
-            raise ValueError("missing FFN weight (w_up, w_down_t, and w_gate for ReGLU)")
+        if "w_up" not in t or "w_down_t" not in t or (self.kind != "relu" and "w_gate" not in t):
+            raise ValueError("missing FFN weight (w_up, w_down_t, and w_gate when gated)")
         t["b_act"] = _dev(w.get("b_act"), torch.float32, "b_act", self.d_ffn)
         for k in ("p_w1", "p_w2"):
             t[k] = _dev(w[k], pd, k, sizes[k])
@@ -606,7 +606,7 @@ def hot_first_permute(w, calib_x, dense_prefix=False):
         out["dense_prefix"] = int((counts == N).sum())  # one synchronisation, at load
     F = int(w["d_ffn"])
     for k in PERMUTED_KEYS:
-        if w.get(k) is not None and (k != "w_gate" or w["kind"] == "reglu"):
+        if w.get(k) is not None and (k != "w_gate" or w["kind"] != "relu"):
             src = w[k]
             if k == "p_w2" and w["p_dtype"] == "fp8":
                 # the codes [d_ffn, r] and the per-row scales move together

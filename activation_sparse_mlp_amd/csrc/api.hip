@@ -388,7 +388,7 @@ spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out)
     if (D.d <= 0 || D.d_ffn <= 0 || D.r <= 0)
         return fail(SPFFN_E_SHAPE, "layer_create: d=%d d_ffn=%d r=%d must be positive", D.d,
                     D.d_ffn, D.r);
-    if (D.kind != SPFFN_RELU && D.kind != SPFFN_REGLU)
+    if (D.kind != SPFFN_RELU && D.kind != SPFFN_REGLU && D.kind != SPFFN_SWIGLU)
         return fail(SPFFN_E_ARG, "layer_create: unknown kind %d", D.kind);
     if (D.w_dtype != SPFFN_F32 && D.w_dtype != SPFFN_F16 && D.w_dtype != SPFFN_Q4_0)
         return fail(SPFFN_E_DTYPE, "layer_create: unknown weight dtype %d", D.w_dtype);
@@ -409,8 +409,8 @@ spffn_status spffn_layer_create(const spffn_layer_desc *desc, spffn_layer **out)
                     D.dense_prefix, D.d_ffn);
     if (!D.w_up || !D.w_down_t || !D.p_w1 || !D.p_b1 || !D.p_w2 || !D.p_b2)
         return fail(SPFFN_E_ARG, "layer_create: a required weight pointer is NULL");
-    if (D.kind == SPFFN_REGLU && !D.w_gate)
-        return fail(SPFFN_E_ARG, "layer_create: ReGLU needs w_gate");
+    if (D.kind != SPFFN_RELU && !D.w_gate)
+        return fail(SPFFN_E_ARG, "layer_create: a gated layer (ReGLU, SwiGLU) needs w_gate");
     const void *ptrs[] = {D.w_gate, D.w_up, D.w_down_t, D.p_w1, D.p_w2};
     for (const void *p : ptrs)
         if (p && !aligned(p, 16))
@@ -768,7 +768,7 @@ spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, 
     if (N < 1) return fail(SPFFN_E_SHAPE, "profile: N=%d < 1", N);
     if (!aligned(x, 16) || !aligned(counts, 4)) return fail(SPFFN_E_ARG, "profile: misaligned");
     const Layer &L = layer->L;
-    const WMat &wa = L.desc.kind == SPFFN_REGLU ? L.gate : L.up;
+    const WMat &wa = L.desc.kind != SPFFN_RELU ? L.gate : L.up;
     SPFFN_HIP(launch_gemv_count(L.desc.w_dtype, wa, L.desc.d_ffn, L.desc.d, x, N, L.desc.b_act,
                                 counts, (hipStream_t)stream),
               "profile launch");

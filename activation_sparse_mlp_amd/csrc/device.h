@@ -101,6 +101,12 @@ __device__ __forceinline__ uint32_t and_word(uint32_t w, uint32_t mask) {
     return r;
 }
 
+// Activation of the activated projection z: ReLU, or for SwiGLU layers the
+// SiLU z * sigmoid(z) = z / (1 + e^-z) (z -> -inf gives -0, z -> +inf gives z).
+__device__ __forceinline__ float gate_act(float z, bool silu) {
+    return silu ? z / (1.0f + __expf(-z)) : fmaxf(z, 0.0f);
+}
+
 // Sum over the 64 lanes, returned to every lane: within each row of 16 lanes
 // by DPP exchanges (pairs, quads, half-row and row mirrors; register-to-register,
 // no LDS round trip), then the four row sums in a fixed order.

@@ -208,6 +208,7 @@ struct UpB1Args {
     const float *h;        // [d]
     const float *scale;    // device RMS scale, or nullptr for 1
     float *act;            // [d_ffn], entry j of the list
+    bool silu;             // SwiGLU: SiLU instead of ReLU on the gate
 };
 
 template <int FMT, bool GATED, int U>
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256) void up_b1_kernel(UpB1Args a) {
             if (lane == 0) {
                 float v = 0.0f;
                 if (valid) {
-                    v = fmaxf(fmaf(vz, s, a.bias ? a.bias[i] : 0.0f), 0.0f);
+                    v = gate_act(fmaf(vz, s, a.bias ? a.bias[i] : 0.0f), a.silu);
                     if constexpr (GATED) v *= vu * s;
                 }
                 a.act[j] = v;
@@ -449,6 +450,7 @@ struct FusedArgs {
     const float *b2;      // [d_ffn]
     float t;
     int kd;               // always-active prefix: rows [0, kd) are not scored
+    bool silu;            // SwiGLU: SiLU instead of ReLU on the gate
     const float *bias;    // [d_ffn] or nullptr
     const float *h;       // [d] residual stream (un-normalised)
     const float *scale;   // device RMS scale
@@ -639,7 +641,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
             uint32_t m = act_mask;
             for (int j = 0; j < k; ++j) m &= m - 1;
             const int kl = __ffs(m) - 1;
-            v = fmaxf(fmaf(vz, s, s_bias[kl]), 0.0f);
+            v = gate_act(fmaf(vz, s, s_bias[kl]), a.silu);
             if constexpr (GATED) v *= vu * s;
             row = g + G * kl;
         }
@@ -909,7 +911,7 @@ hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, cons
                         const int32_t *count, float *act, hipStream_t s) {
     const spffn_layer_desc &D = L.desc;
     UpB1Args a{};
-    const bool gated = D.kind == SPFFN_REGLU;
+    const bool gated = D.kind != SPFFN_RELU;
     a.wa = gated ? L.gate : L.up;
     a.wu = L.up;
     a.bias = D.b_act;
@@ -920,6 +922,7 @@ hipError_t launch_up_b1(const Layer &L, const float *h, const float *scale, cons
     a.h = h;
     a.scale = scale;
     a.act = act;
+    a.silu = D.kind == SPFFN_SWIGLU;
     int blocks = (D.d_ffn + 3) / 4;
     if (blocks > kUpB1MaxBlocks) blocks = kUpB1MaxBlocks;
     const int E = packet_elems(D.w_dtype);
@@ -998,7 +1001,7 @@ template <int FMT, bool GATED> constexpr int fused_rw() {
 
 int fused_rows_per_group(const Layer &L) {
     return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4
-                : L.desc.kind == SPFFN_REGLU  ? kFusedRW
+                : L.desc.kind != SPFFN_RELU   ? kFusedRW
                                               : kFusedRWNonGated);
 }
 int fused_groups(const Layer &L) {
@@ -1091,7 +1094,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
                            int32_t *done, float *part, int32_t *chunk_cnt, int32_t *giveups,
                            bool adapt, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const spffn_layer_desc &D = L.desc;
-    const bool gated = D.kind == SPFFN_REGLU;
+    const bool gated = D.kind != SPFFN_RELU;
     const int G = fused_groups(L), UA = fused_ua(L), C = fused_chunks(L), NG = fused_per_chunk(L);
     const int slices = down_slices(L);
     FusedArgs f{};
@@ -1106,6 +1109,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     f.b2 = D.p_b2;
     f.t = L.t;
     f.kd = D.dense_prefix;
+    f.silu = D.kind == SPFFN_SWIGLU;
     f.adapt = adapt;
     f.bias = D.b_act;
     f.h = h;

@@ -29,6 +29,7 @@ struct UpArgs {
     int B;
     float *act;  // [B, d_ffn] (row stride d_ffn), entry j of the list
     int chunk_packets;
+    bool silu;   // SwiGLU: SiLU instead of ReLU on the gate
 };
 
 template <int FMT, int NB, bool GATED, int U>
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kUpWaves * kWave) void ffn_up_kernel(UpArgs a) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     if (b < a.B) {
-                        float v = fmaxf(za[b] + bias, 0.0f);
+                        float v = gate_act(za[b] + bias, a.silu);
                         if constexpr (GATED) v *= zu[b];
                         a.act[(size_t)b * a.d_ffn + j] = valid ? v : 0.0f;
                     }
@@ -236,7 +237,7 @@ static hipError_t up_dispatch(const Layer &L, UpArgs &a, hipStream_t s) {
     const size_t lds = (size_t)a.chunk_packets * per_packet;
     int blocks = (a.d_ffn + kUpWaves - 1) / kUpWaves;
     if (blocks > 2048) blocks = 2048;
-    if (L.desc.kind == SPFFN_REGLU)
+    if (L.desc.kind != SPFFN_RELU)
         ffn_up_kernel<FMT, NB, true, 4><<<blocks, kUpWaves * kWave, lds, s>>>(a);
     else
         ffn_up_kernel<FMT, NB, false, 8><<<blocks, kUpWaves * kWave, lds, s>>>(a);
@@ -255,10 +256,11 @@ static hipError_t up_dispatch_nb(const Layer &L, UpArgs &a, hipStream_t s) {
 hipError_t launch_ffn_up(const Layer &L, const float *x, int B, const int32_t *idx,
                          const int32_t *count, float *act, hipStream_t s) {
     UpArgs a{};
-    const bool gated = L.desc.kind == SPFFN_REGLU;
+    const bool gated = L.desc.kind != SPFFN_RELU;
     a.wa = gated ? L.gate : L.up;
     a.wu = L.up;
     a.bias = L.desc.b_act;
+    a.silu = L.desc.kind == SPFFN_SWIGLU;
     a.d = L.desc.d;
     a.d_ffn = L.desc.d_ffn;
     a.idx = idx;

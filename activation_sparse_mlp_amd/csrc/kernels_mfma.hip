@@ -153,6 +153,7 @@ struct BgArgs {
     _Float16 *ahi, *alo;   // act: [B, ld_act], entry j of the list
     int ld_act;
     const float *tsc;      // act: per-token scale of the products (raw input), or nullptr
+    bool silu;             // act: SwiGLU (SiLU instead of ReLU on the gate)
 };
 
 template <int WV, int T, bool GATED, bool SPLIT2, int EPI>
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                 if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
             } else {
                 const float sc = a.tsc ? a.tsc[n] : 1.0f;
-                float v = fmaxf(fmaf(za, sc, a.bias ? a.bias[rr] : 0.0f), 0.0f);
+                float v = gate_act(fmaf(za, sc, a.bias ? a.bias[rr] : 0.0f), a.silu);
                 if constexpr (GATED) v *= zu * sc;
                 const _Float16 h = (_Float16)v;
                 a.ahi[(size_t)n * a.ld_act + jj] = h;
@@ -709,13 +710,14 @@ static hipError_t mfma_ffn(const Layer &L, BgArgs a, dim3 grid, const int32_t *i
                            const int32_t *count, int B, float *part, hipStream_t s) {
     // a.tsc (if set) scales the products per token
     const spffn_layer_desc &D = L.desc;
-    const bool gated = D.kind == SPFFN_REGLU;
+    const bool gated = D.kind != SPFFN_RELU;
     a.wa = reinterpret_cast<const _Float16 *>((gated ? L.gate : L.up).data);
     a.wu = reinterpret_cast<const _Float16 *>(L.up.data);
     a.K = D.d;
     a.rows = D.d_ffn;
     a.B = B;
     a.bias = D.b_act;
+    a.silu = D.kind == SPFFN_SWIGLU;
     if (gated) launch_bg<true, kEpiAct, kGatherWavesG, kGatherWavesG / 2>(a, grid, s);
     else launch_bg<false, kEpiAct, kGatherWaves, kGatherWaves / 2>(a, grid, s);
 

@@ -91,7 +91,7 @@ def step_bytes(layers, counts, B):
     for L, u in zip(layers, counts):
         wp, ps = pred_bytes(L)
         row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
-        n_mat = 3 if L.kind == "reglu" else 2
+        n_mat = 2 if L.kind == "relu" else 3
         kd = getattr(L, "dense_prefix", 0)  # always-active rows are not scored
         total += (L.r * L.d + (L.d_ffn - kd) * L.r) * wp + (4 + ps) * (L.r + L.d_ffn - kd)
         total += int(u) * (n_mat * row + 4 + 4)
@@ -110,7 +110,7 @@ def dominant_kernel_bytes(L, u, B):
     writes are workspace traffic, not counted."""
     wp, ps = pred_bytes(L)
     row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
-    n_mat = 3 if L.kind == "reglu" else 2
+    n_mat = 2 if L.kind == "relu" else 3
     kd = getattr(L, "dense_prefix", 0)  # always-active rows are not scored
     return ((L.d_ffn - kd) * (L.r * wp + ps + 4) + L.d_ffn + int(u) * (n_mat * row + 4 + 8)
             + B * (L.r + L.d) * 4)
@@ -160,7 +160,7 @@ def batched_ffn_bytes(L, u, B):
     pair brackets them when B > 1): the u listed rows of every FFN matrix, their
     biases and index entries, the tokens' inputs and the residual in/out."""
     row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
-    n_mat = 3 if L.kind == "reglu" else 2
+    n_mat = 2 if L.kind == "relu" else 3
     return int(u) * (n_mat * row + 4 + 4) + B * 3 * L.d * 4
 
 
@@ -197,7 +197,7 @@ def dense_step_bytes(layers, B):
     total = 0
     for L in layers:
         row = L.d * 4 if L.w_dtype == "f32" else L.d * 2 if L.w_dtype == "f16" else L.d // 32 * 18
-        n_mat = 3 if L.kind == "reglu" else 2
+        n_mat = 2 if L.kind == "relu" else 3
         total += L.d_ffn * (n_mat * row + 4) + B * 2 * L.d * 4
     return total
 

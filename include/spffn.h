@@ -75,8 +75,16 @@ typedef enum {
 } spffn_dtype;
 
 typedef enum {
-    SPFFN_RELU = 0,  /* non-gated: a_i = max(W_up[i] . x + b_i, 0)               */
-    SPFFN_REGLU = 1  /* gated:     a_i = max(W_gate[i] . x + b_i, 0) * (W_up[i] . x) */
+    SPFFN_RELU = 0,   /* non-gated: a_i = max(W_up[i] . x + b_i, 0)               */
+    SPFFN_REGLU = 1,  /* gated:     a_i = max(W_gate[i] . x + b_i, 0) * (W_up[i] . x) */
+    SPFFN_SWIGLU = 2  /* gated:     a_i = silu(W_gate[i] . x + b_i) * (W_up[i] . x),
+                         silu(z) = z / (1 + e^-z).  SiLU is never exactly 0, so the
+                         neurons left out are near zero rather than zero: the
+                         sparse FFN approximates the dense one, by at most the
+                         skipped |a_i| times their W_down column norms (Guide,
+                         "The Hidden Inefficiency": SwiGLU activations have
+                         near-zero magnitudes, not exact zeros).  "Active" for
+                         profiling is a positive gate pre-activation.          */
 } spffn_kind;
 
 /* Maximum number of tokens per call (batch B). */

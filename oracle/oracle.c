@@ -31,6 +31,7 @@
 
 #define OR_RELU 0
 #define OR_REGLU 1
+#define OR_SWIGLU 2
 
 #define Q4_0_BLOCK 32
 #define Q4_0_BYTES 18
@@ -218,14 +219,15 @@ void oracle_union(const uint8_t *masks, int64_t B, int64_t n, uint8_t *out)
 /* Pre-activations of neuron i ([Guide] "The Hidden Inefficiency", the FFN
  * equation; bias b_i only on the activated projection):
  *   ReLU  (non-gated):  z_i = W_up[i] . x + b_i,   u_i = 1 (unused)
- *   ReGLU (gated):      z_i = W_gate[i] . x + b_i, u_i = W_up[i] . x
- * The activation is a_i = max(z_i, 0) (ReLU) or max(z_i, 0) * u_i (ReGLU). */
+ *   ReGLU, SwiGLU (gated): z_i = W_gate[i] . x + b_i, u_i = W_up[i] . x
+ * The activation is a_i = max(z_i, 0) (ReLU), max(z_i, 0) * u_i (ReGLU) or
+ * silu(z_i) * u_i (SwiGLU), silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
 static double neuron_act(int kind, int w_dtype, int64_t d, int64_t d_ffn,
                          const void *W_gate, const void *W_up, const float *b,
                          const double *x, int64_t i, double *row, double *z_out)
 {
     double z, u = 1.0;
-    if (kind == OR_REGLU) {
+    if (kind != OR_RELU) {
         oracle_deq_row(W_gate, w_dtype, d_ffn, d, i, row);
         z = dot(row, x, d) + (b ? (double)b[i] : 0.0);
         oracle_deq_row(W_up, w_dtype, d_ffn, d, i, row);
@@ -236,13 +238,13 @@ static double neuron_act(int kind, int w_dtype, int64_t d, int64_t d_ffn,
     }
     if (z_out)
         *z_out = z;
-    double a = z > 0.0 ? z : 0.0;
-    return kind == OR_REGLU ? a * u : a;
+    double a = kind == OR_SWIGLU ? z / (1.0 + exp(-z)) : (z > 0.0 ? z : 0.0);
+    return kind != OR_RELU ? a * u : a;
 }
 
 static int check_layer(int kind, int w_dtype, int64_t d)
 {
-    if (kind != OR_RELU && kind != OR_REGLU)
+    if (kind != OR_RELU && kind != OR_REGLU && kind != OR_SWIGLU)
         return -1;
     if (w_dtype != OR_F32 && w_dtype != OR_F16 && w_dtype != OR_Q4_0)
         return -1;
@@ -348,7 +350,7 @@ int oracle_preact(int kind, int w_dtype, int64_t d, int64_t d_ffn,
         return -2;
     for (i = 0; i < d_ffn; ++i) {
         double zi;
-        if (kind == OR_REGLU) {
+        if (kind != OR_RELU) {
             oracle_deq_row(W_gate, w_dtype, d_ffn, d, i, row);
             zi = dot(row, x, d) + (b ? (double)b[i] : 0.0);
             if (u) {
@@ -379,7 +381,7 @@ int oracle_profile(int kind, int w_dtype, int64_t d, int64_t d_ffn,
     int64_t i, t;
     if (check_layer(kind, w_dtype, d))
         return -1;
-    const void *W_act = (kind == OR_REGLU) ? W_gate : W_up;
+    const void *W_act = (kind != OR_RELU) ? W_gate : W_up;
     double *row = (double *)malloc(sizeof(double) * (size_t)d);
     if (!row)
         return -2;

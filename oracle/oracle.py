@@ -2,7 +2,8 @@
 
 A layer is a plain dict of numpy arrays and ints:
 
-  kind      "relu" (non-gated up/down) or "reglu" (gated)
+  kind      "relu" (non-gated up/down), "reglu" or "swiglu" (gated; SiLU
+            on the gate for SwiGLU)
   w_dtype   "f32" | "f16" | "q4_0"   storage of w_gate / w_up / w_down_t
   p_dtype   "f32" | "f16" | "fp8"    storage of p_w1 / p_w2
   d, d_ffn, r
@@ -34,7 +35,7 @@ import numpy as np
 from . import LIB, build
 
 _DT = {"f32": 0, "f16": 1, "q4_0": 2, "fp8": 3}
-_KIND = {"relu": 0, "reglu": 1}
+_KIND = {"relu": 0, "reglu": 1, "swiglu": 2}
 
 _lib = None
 
@@ -191,7 +192,7 @@ def logit_threshold(tau):
 # FFN
 # --------------------------------------------------------------------------- #
 def _ffn_args(L):
-    wg = _c(L["w_gate"]) if L["kind"] == "reglu" else None
+    wg = _c(L["w_gate"]) if L["kind"] != "relu" else None
     wu, wd = _c(L["w_up"]), _c(L["w_down_t"])
     b = _c(L["b_act"], np.float32) if L.get("b_act") is not None else None
     return wg, wu, wd, b

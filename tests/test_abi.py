@@ -61,6 +61,8 @@ def create(**kw):
     ({"d_ffn": -1}, E_SHAPE),
     ({"r": 0}, E_SHAPE),
     ({"kind": 7}, E_ARG),
+    ({"kind": 2}, OK),                      # SwiGLU
+    ({"kind": 2, "w_gate": None}, E_ARG),   # gated: needs the gate
     ({"w_dtype": 9}, E_DTYPE),
     ({"p_dtype": 2}, E_DTYPE),
     ({"d": 260}, E_SHAPE),                  # fp16 rows need d % 8 == 0

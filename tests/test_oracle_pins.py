@@ -91,6 +91,57 @@ def test_dense_prefix_invariants():
     assert np.array_equal(oracle.ffn_masked(L, n, pre), oracle.ffn_dense(L, n)[0])
 
 
+def _swiglu_hand():
+    g = load_golden("hand_swiglu.json")
+    f = lambda v: np.asarray(v, dtype=np.float32)  # noqa: E731
+    L = dict(kind="swiglu", w_dtype="f32", p_dtype="f32", d=2, d_ffn=3, r=1,
+             w_gate=f(g["w_gate"]), w_up=f(g["w_up"]), w_down_t=f(g["w_down_t"]),
+             b_act=f(g["b_act"]), p_w1=f([[0, 0]]), p_b1=f([0]), p_w2=f([[0], [0], [0]]),
+             p_b2=f([1, 1, 1]), t=0.0)
+    x = np.array([math.log(3.0), 2.0])
+    return g, L, x
+
+
+def test_swiglu_hand():
+    """SiLU on the hand-derived layer (golden/hand_swiglu.json): the
+    activations, the dense output, and a mask that leaves a near-zero neuron
+    out, whose error is exactly that neuron's contribution."""
+    g, L, x = _swiglu_hand()
+    ln3 = math.log(3.0)
+    y, act = oracle.ffn_dense(L, x)
+    np.testing.assert_allclose(act, ln3 * np.array(g["act_over_ln3"]), rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(y, ln3 * np.array(g["y_over_ln3"]), rtol=1e-15, atol=1e-16)
+    y01 = oracle.ffn_masked(L, x, np.uint8([1, 1, 0]))
+    np.testing.assert_allclose(y01, ln3 * np.array(g["y_mask01_over_ln3"]), rtol=1e-15,
+                               atol=1e-16)
+    # every neuron: the masked FFN is the dense one bit for bit
+    assert np.array_equal(oracle.ffn_masked(L, x, np.ones(3, np.uint8)), y)
+
+
+def test_swiglu_silu_against_expit_and_magnitude_bound():
+    """SiLU against scipy's logistic function (a library the oracle does not
+    use); the magnitude mask {|a_i| > eps} loses at most the skipped |a_i|
+    times their W_down column norms, and reproduces the dense FFN as eps -> 0."""
+    special = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(31)
+    L = _rand_layer(rng, "reglu", 24, 60, r=8)
+    L["kind"] = "swiglu"
+    L["w_gate"] = (L["w_gate"] * 6).astype(np.float32)  # wide gate: magnitude-sparse
+    x = rng.standard_normal(24)
+    z, u, _ = oracle.preact(L, x)
+    y, act = oracle.ffn_dense(L, x)
+    np.testing.assert_allclose(act, z * special.expit(z) * u, rtol=1e-13, atol=1e-300)
+    W = oracle.deq(L["w_down_t"], "f32", 24)
+    for eps in (1e-1, 1e-2, 1e-3):
+        M = (np.abs(act) > eps).astype(np.uint8)
+        err = np.linalg.norm(oracle.ffn_masked(L, x, M) - y)
+        bound = np.sum(np.abs(act[M == 0]) * np.linalg.norm(W[M == 0], axis=1))
+        assert err <= bound * (1 + 1e-12) + 1e-15, (eps, err, bound)
+        assert M.sum() < 60  # something was skipped
+    M0 = (act != 0).astype(np.uint8)
+    np.testing.assert_allclose(oracle.ffn_masked(L, x, M0), y, rtol=1e-14, atol=1e-300)
+
+
 def test_e4m3_decode_all_codes():
     """Every OCP E4M3 code against torch's float8_e4m3fn widening (a library
     the oracle does not use), and hand values from the format's definition:

@@ -153,3 +153,23 @@ def test_fp8_predictor_layer():
     X = make_tokens(d, 64, 1, seed=5)[:, 0, :].double().numpy()
     dens = np.mean([oracle.predict(L, x)[2].mean() for x in X])
     assert abs(dens - cfg.mean_activity) < 0.03, dens
+
+
+def test_swiglu_layer_is_magnitude_sparse():
+    """The SwiGLU workload's wide gate makes SiLU activations magnitude-sparse:
+    few neurons exceed 1e-3 of the token's largest activation, while the
+    predictor keeps the configured density."""
+    from dataclasses import replace
+
+    from workloads import LLAMA2_7B_SWIGLU
+    cfg = replace(LLAMA2_7B_SWIGLU, d=512, d_ffn=1536, r=64, gate_std=0.1 * 8 ** 0.5)
+    L = layer_to_numpy(make_layer(cfg, 0, seed=0, n_cal=2048))
+    L["t"] = oracle.logit_threshold(L["tau"])
+    X = make_tokens(cfg.d, 16, 1, seed=3)[:, 0, :].double().numpy()
+    mag, dens = [], []
+    for x in X:
+        _, act = oracle.ffn_dense(L, x)
+        mag.append(np.mean(np.abs(act) > 1e-3 * np.abs(act).max()))
+        dens.append(oracle.predict(L, x)[2].mean())
+    assert np.mean(mag) < 0.25, np.mean(mag)
+    assert abs(np.mean(dens) - cfg.mean_activity) < 0.03, np.mean(dens)

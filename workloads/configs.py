@@ -15,7 +15,7 @@ from typing import Tuple
 @dataclass(frozen=True)
 class Config:
     name: str
-    kind: str            # "relu" (non-gated up/down) or "reglu" (gated)
+    kind: str            # "relu" (non-gated up/down), "reglu" or "swiglu" (gated)
     d: int
     d_ffn: int
     layers: int
@@ -27,6 +27,7 @@ class Config:
     tokens: int
     batches: Tuple[int, ...] = (1,)
     w_std: float = 0.02  # std of fp weights (fp32 / fp16 configs)
+    gate_std: float = 0.0  # std of the gate matrix when set (else w_std)
     q4_scale_std: float = 0.003  # std of the |N(0, s^2)| block scales (q4_0)
     tau: float = 0.5
     hot_first: bool = False
@@ -43,6 +44,16 @@ LLAMA2_7B = Config(
     name="llama2_7b_reglu", kind="reglu", d=4096, d_ffn=11008, layers=32, w_dtype="f16",
     p_dtype="f16", r=1024, gamma=1.2, mean_activity=0.10, tokens=128,
     description="Llama2-7B-shaped ReGLU FFN (ProSparse-like), fp16")
+
+# SwiGLU: SiLU is never exactly zero, so the gate weights are wider (std 0.1,
+# ||w_gate|| ~ 6.4) to make the activation magnitude-sparse: a neuron whose
+# gate pre-activation sits a typical distance below zero has |silu(z)| of
+# about 1e-3 and below ([Guide] "The Hidden Inefficiency": SwiGLU
+# activations are near-zero magnitudes rather than exact zeros).
+LLAMA2_7B_SWIGLU = Config(
+    name="llama2_7b_swiglu", kind="swiglu", d=4096, d_ffn=11008, layers=32, w_dtype="f16",
+    p_dtype="f16", r=1024, gamma=1.2, mean_activity=0.10, tokens=128, gate_std=0.1,
+    description="Llama2-7B-shaped SwiGLU FFN (magnitude-sparse gate), fp16")
 
 FALCON_40B = Config(
     name="falcon_40b_relu", kind="relu", d=8192, d_ffn=32768, layers=60, w_dtype="f16",
@@ -78,5 +89,5 @@ OPT_175B_Q4 = Config(
     p_dtype="f16", r=1024, gamma=1.3, mean_activity=0.05, tokens=128,
     description="OPT-175B-shaped ReLU FFN with 4-bit (Q4_0 block) weights, fp16 predictor")
 
-ALL = {c.name: c for c in (TINY, LLAMA2_7B, FALCON_40B, LLAMA2_70B, LLAMA2_70B_FP8P,
-                           LLAMA2_70B_PREFIX, OPT_175B_Q4)}
+ALL = {c.name: c for c in (TINY, LLAMA2_7B, LLAMA2_7B_SWIGLU, FALCON_40B, LLAMA2_70B,
+                           LLAMA2_70B_FP8P, LLAMA2_70B_PREFIX, OPT_175B_Q4)}

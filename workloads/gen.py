@@ -108,8 +108,9 @@ def _pred_store(w, p_dtype):
     return w, w
 
 
-def _weights(cfg, g_codes_or_normal, g_scales, shape, device):
-    """(stored tensor, fp32 values) of one weight matrix."""
+def _weights(cfg, g_codes_or_normal, g_scales, shape, device, std=None):
+    """(stored tensor, fp32 values) of one weight matrix (fp: std, default
+    the config's w_std)."""
     rows, cols = shape
     if cfg.w_dtype == "q4_0":
         codes = torch.randint(0, 16, shape, generator=g_codes_or_normal, device=device,
@@ -118,7 +119,7 @@ def _weights(cfg, g_codes_or_normal, g_scales, shape, device):
                   * cfg.q4_scale_std).abs().half()
         vals = q4_0_values(codes, scales)
         return q4_0_pack(codes, scales), vals
-    w = torch.randn(shape, generator=g_codes_or_normal, device=device) * cfg.w_std
+    w = torch.randn(shape, generator=g_codes_or_normal, device=device) * (std or cfg.w_std)
     if cfg.w_dtype == "f16":
         w = w.half()
         return w, w.float()
@@ -148,11 +149,12 @@ def make_layer(cfg: Config, layer: int, seed: int = 0, device="cpu", n_cal: int 
     p = p_rank[order.numpy()]
 
     def w(tag):
+        std = cfg.gate_std if tag == TAG_GATE and cfg.gate_std else None
         return _weights(cfg, _gen(dev, seed, layer, tag), _gen(dev, seed, layer, tag + 40),
-                        (F, d), dev)
+                        (F, d), dev, std)
 
     up_vals = None
-    if cfg.kind == "reglu":
+    if cfg.kind != "relu":
         w_gate, act_vals = w(TAG_GATE)
         w_up, up_vals = w(TAG_UP)
     else:
@@ -242,9 +244,9 @@ def _carry(w, n):
     [N, d]: its FFN over the neurons its own predictor selects (fp32; the
     generator's propagation only, never an expected value)."""
     z = n @ w["act_values"].t() + w["b_act"]
-    a = torch.relu(z)
+    a = torch.nn.functional.silu(z) if w["kind"] == "swiglu" else torch.relu(z)
     del z
-    if w["kind"] == "reglu":
+    if w["kind"] != "relu":
         a = a * (n @ w["up_values"].t())
     hid = torch.relu(n @ w["p_w1_values"].t() + w["p_b1"])
     logit = hid @ w["p_w2_values"].t() + w["p_b2"]
