@@ -571,14 +571,18 @@ def q4_0_repack(aos, rows, cols, soa=None):
     return soa
 
 
+STREAM_SINK_WORDS = 4096
+
+
 def stream_read(buf, sink=None):
     """Read every byte of a device tensor once (bandwidth probe); returns the
-    device uint32 sink the data is folded into."""
+    device int32 [4096] sink the data is folded into (the XOR of its words is
+    the XOR of all 32-bit words of buf)."""
     buf = _dev(buf, None, "buf")
     nbytes = buf.numel() * buf.element_size()
     if sink is None:
-        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
-    _dev(sink, torch.int32, "sink", 1, at_least=True)
+        sink = torch.zeros(STREAM_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _dev(sink, torch.int32, "sink", STREAM_SINK_WORDS, at_least=True)
     _check(load().spffn_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()),
            "spffn_stream_read")
     return sink

@@ -280,15 +280,20 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // stream read (measurement only): every 16-byte word of a buffer is read once
-// with a non-temporal load, 8 loads in flight per thread; each workgroup folds
-// its words with XOR and XORs the result into *sink, so no load can be
-// dropped.  Its bandwidth is the read ceiling the decode kernels are compared
-// with.
+// with a non-temporal load, 8 loads in flight per thread, 4096 workgroups in a
+// grid-stride loop; each workgroup folds its words with XOR and stores the
+// result to its own sink word (no atomics: thousands of them on one address
+// would serialise at the end of the launch), so no load can be dropped.  Its
+// bandwidth is the read ceiling the decode kernels are compared with.
 // ---------------------------------------------------------------------------
 typedef unsigned int stream_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kStreamSinkWords = SPFFN_STREAM_SINK_WORDS;
 
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p,
                                                           int64_t n16, uint32_t *sink) {
+    // sink words no workgroup owns are cleared by workgroup 0
+    if (blockIdx.x == 0)
+        for (int k = gridDim.x + threadIdx.x; k < kStreamSinkWords; k += blockDim.x) sink[k] = 0;
     constexpr int U = 8;
     __shared__ uint32_t red[4];
     uint32_t acc = 0;
@@ -309,13 +314,13 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
     __syncthreads();
-    if (threadIdx.x == 0) atomicXor(sink, red[0] ^ red[1] ^ red[2] ^ red[3]);
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s) {
     const int64_t n16 = bytes / 16;
     int64_t blocks = (n16 + 256 * 8 - 1) / (256 * 8);
-    if (blocks > 2048) blocks = 2048;  // eight workgroups per CU, grid-stride beyond that
+    if (blocks > kStreamSinkWords) blocks = kStreamSinkWords;  // grid-stride beyond that
     if (blocks < 1) blocks = 1;
     stream_read_kernel<<<(int)blocks, 256, 0, s>>>(static_cast<const uint4 *>(buf), n16, sink);
     return hipGetLastError();

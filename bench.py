@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=8)
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed repetitions of the K steps (the first is the headline)")
-    ap.add_argument("--stream-gib", type=float, default=2.0,
+    ap.add_argument("--stream-gib", type=float, default=4.0,
                     help="buffer size of the read-bandwidth ceiling probe (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -482,7 +482,7 @@ def main():
     if args.stream_gib > 0:
         nbytes = int(args.stream_gib * 2**30) // 16 * 16
         buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        sink = torch.zeros(spffn._lib.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
         for _ in range(2):
             spffn.stream_read(buf, sink)
         torch.cuda.synchronize()

@@ -358,11 +358,13 @@ spffn_status spffn_q4_0_repack(const void *aos, void *soa, int32_t rows, int32_t
 
 /* Read-bandwidth probe: reads every byte of buf [bytes] once with 16-byte
  * non-temporal loads (the access the decode kernels use for weights) and
- * XORs a fold of the data into *sink (a device uint32, so the loads cannot
- * be dropped; its value has no meaning).  Timed over a buffer much larger
- * than the caches it gives the read ceiling that the decode step's achieved
- * bandwidth is compared with.  bytes a positive multiple of 16; buf 16-byte
- * aligned.  SPFFN_E_ARG / SPFFN_E_SHAPE otherwise. */
+ * folds the data into sink [SPFFN_STREAM_SINK_WORDS] (device uint32s: the
+ * XOR of all sink words is the XOR of all 32-bit words of buf), so the loads
+ * cannot be dropped.  Timed over a buffer much larger than the caches it
+ * gives the read ceiling that the decode step's achieved bandwidth is
+ * compared with.  bytes a positive multiple of 16; buf 16-byte aligned.
+ * SPFFN_E_ARG / SPFFN_E_SHAPE otherwise. */
+#define SPFFN_STREAM_SINK_WORDS 4096
 spffn_status spffn_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
 /* [host] Test hook.  Inside the single-token decode step, the workgroups that

@@ -26,4 +26,5 @@ def test_stream_read_reads_every_word(nbytes):
     sink = spffn.stream_read(buf)
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
-    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(want)
