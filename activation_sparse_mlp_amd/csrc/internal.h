@@ -133,7 +133,7 @@ hipError_t launch_reduce_split(const float *part, int chunks, int B, int d, cons
                                float *y, _Float16 *hi, _Float16 *lo, float *ss, hipStream_t s);
 
 // y = resid + sum_c part[c]; optionally *total_out = sum of chunk_cnt[0..chunks)
-// and zero[k * zero_stride] = 0 for k < n_zero
+// and zero[k * zero_stride + {0, 1}] = 0 for k < n_zero (64-bit counters)
 hipError_t launch_reduce_groups(const float *part, int chunks, int64_t n, const float *resid,
                                 float *y, hipStream_t s, const int32_t *chunk_cnt = nullptr,
                                 int32_t *total_out = nullptr, int32_t *zero = nullptr,

@@ -407,8 +407,12 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
         for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
         if (threadIdx.x == 0) *total_out = c;
     }
+    // (each chunk counter is 64 bits: two words)
     if (blockIdx.x == 0)
-        for (int k = threadIdx.x; k < n_zero; k += blockDim.x) zero[(size_t)k * zero_stride] = 0;
+        for (int k = threadIdx.x; k < n_zero; k += blockDim.x) {
+            zero[(size_t)k * zero_stride] = 0;
+            zero[(size_t)k * zero_stride + 1] = 0;
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -459,7 +463,8 @@ struct FusedArgs {
     int32_t *lst_i;       // [G*RB]
     float *lst_a;         // [G*RB]
     int per_chunk;        // NG: consecutive groups per down-projection chunk
-    int32_t *done;        // [C * kDoneStride] groups published per chunk (zero at launch)
+    int32_t *done;        // [C * kDoneStride] per chunk, 64 bits: groups published (low
+                          // word), groups with active rows (high word); zero at launch
     bool adapt;           // host only: the token's threshold is at scale[1], not t
 };
 
@@ -627,6 +632,18 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         }
     }
     __syncthreads();
+    // Publish.  The chunk's 64-bit counter gains 1 per group (low word) and,
+    // for a group with active rows, that group's bit (bit 32 + its index in
+    // the chunk): a group without active rows writes no list slots and does
+    // not wait for any store, and the down projection reads only the slots of
+    // flagged groups.  (n_act is the same in every thread.)
+    unsigned long long *const cnt64 = reinterpret_cast<unsigned long long *>(
+        a.done + (size_t)(g / a.per_chunk) * kDoneStride);
+    if (n_act == 0) {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(cnt64, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     if ((int)threadIdx.x < RB) {
         const int k = threadIdx.x;
         int row = -1;
@@ -660,7 +677,7 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_sched_barrier(0);
         if (lane == 0)
-            __hip_atomic_fetch_add(a.done + (size_t)(g / a.per_chunk) * kDoneStride, 1,
+            __hip_atomic_fetch_add(cnt64, 1ull + (1ull << (32 + g % a.per_chunk)),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -685,11 +702,11 @@ struct DownListArgs {
     int32_t *giveups;      // device count of workgroups that gave up waiting
 };
 
-constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 64, rows per group <= 20
+constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 32, rows per group <= 20
 
 template <int FMT, int UR>
 __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slice, const int c,
-                                           const bool ready) {
+                                           const bool ready, const uint32_t gmask) {
     constexpr int E = PacketElems<FMT>::value;
     constexpr int SPT = kDownListMaxSlots / 256;  // slots per thread
     __shared__ float red[4 * 64 * E <= kDownListMaxSlots ? 1 : 64 * E];
@@ -701,7 +718,7 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
     const int p = slice * 64 + lane;
     const bool pv = p < NP;
     const int g0 = c * a.per_chunk;
-    const int ng = min(a.per_chunk, a.G - g0);  // groups of this chunk, at most 64 (launcher)
+    const int ng = min(a.per_chunk, a.G - g0);  // groups of this chunk, at most 32 (launcher)
     const int S = ng * a.RB;                     // slots of this chunk
     const size_t base = (size_t)g0 * a.RB;
     const int col0 = slice * 64 * E;
@@ -722,13 +739,15 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         // agent-scope loads: they see the row groups' agent-scope stores
+        // only the slots of groups that flagged active rows were written
         const int sl = (int)threadIdx.x + 256 * u;
-        vi[u] = sl < S ? __hip_atomic_load(a.lst_i + base + sl, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : -1;
-        va[u] = sl < S ? __hip_atomic_load(a.lst_a + base + sl, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : 0.0f;
+        const bool live = sl < S && ((gmask >> (sl / a.RB)) & 1u);
+        vi[u] = live ? __hip_atomic_load(a.lst_i + base + sl, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : -1;
+        va[u] = live ? __hip_atomic_load(a.lst_a + base + sl, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.0f;
     }
     // compaction of the active slots, in slot order
     int T = 0;
@@ -841,22 +860,29 @@ __global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer
     const int c = q / slices, slice = q - c * slices;
     const int need = min(dn.per_chunk, dn.G - c * dn.per_chunk);
     __shared__ int s_ready;
+    __shared__ uint32_t s_gmask;
     if (threadIdx.x == 0) {
+        const unsigned long long *cnt64 =
+            reinterpret_cast<const unsigned long long *>(f.done + (size_t)c * kDoneStride);
         int ok = 0;
+        uint32_t gm = 0;
         for (int it = 0; it < dn.wait_polls; ++it) {
-            if (__hip_atomic_load(f.done + (size_t)c * kDoneStride, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT) >= need) {
+            const unsigned long long v =
+                __hip_atomic_load(cnt64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((int)(uint32_t)v >= need) {
                 ok = 1;
+                gm = (uint32_t)(v >> 32);  // groups of the chunk with active rows
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
         }
         s_ready = ok;
+        s_gmask = gm;
     }
     // every wave issues its slot loads after this barrier, so after the count
     // was seen complete
     __syncthreads();
-    down_chunk<FMT, UR>(dn, slice, c, s_ready != 0);
+    down_chunk<FMT, UR>(dn, slice, c, s_ready != 0, s_gmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -991,8 +1017,8 @@ constexpr int kFusedRWNonGated = 3;
 // (measured at the 175B-shaped layer: 8 rows 55.5 us, 12 rows 51.4, 16 rows
 // 50.4-51.2, 20 rows 48.0-48.7, 24 rows 55.2, 28 rows 49.7, 32 rows 52.4).
 constexpr int kFusedRWQ4 = 5;
-static_assert(4 * kFusedRW * 64 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 64 <= kDownListMaxSlots &&
-                  4 * kFusedRWNonGated * 64 <= kDownListMaxSlots,
+static_assert(4 * kFusedRW * 32 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 32 <= kDownListMaxSlots &&
+                  4 * kFusedRWNonGated * 32 <= kDownListMaxSlots,
               "a down-projection chunk must hold its groups' list slots");
 
 template <int FMT, bool GATED> constexpr int fused_rw() {
@@ -1009,8 +1035,9 @@ int fused_groups(const Layer &L) {
     return (L.desc.d_ffn + RB - 1) / RB;
 }
 
-// Down-projection chunks: ranges of NG consecutive row groups, NG <= 64 (so a
-// chunk's slots fit the down workgroup's LDS list), at least 128 chunks (192
+// Down-projection chunks: ranges of NG consecutive row groups, NG <= 32 (one
+// flag bit per group in the chunk counter; a chunk's slots fit the down
+// workgroup's LDS list), at least 128 chunks (192
 // for 4-bit rows) when there are that many groups: smaller chunks complete
 // sooner after their last group, more of them cost more partial sums.
 // Measured per step, 70B shape: 32 chunks 4.15 ms, 64 3.87, 96 3.86, 128
@@ -1019,7 +1046,7 @@ int fused_groups(const Layer &L) {
 int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
     const int cmin = L.desc.w_dtype == SPFFN_Q4_0 ? 192 : 128;
-    int c = (G + 63) / 64;
+    int c = (G + 31) / 32;  // at most 32 groups: one flag bit each in the counter
     if (c < cmin) c = cmin;
     if (c > G) c = G;
     return (G + c - 1) / c;
