@@ -3,7 +3,7 @@
 // normalisation, barriers), so the 128-bit streaming loads overlap them.
 //
 // Decode step, per layer (three kernels):
-//   w1_b1        hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps)
+//   w1x_b1       hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps)
 //   layer_b1     row groups: logit = W2 . hid + b2, mask = logit > t, and for
 //                the active rows of each 8-row group act = max(z, 0) [* u]
 //                with z = (W_act[i] . h) * s + b_i, listed per group;
@@ -11,7 +11,7 @@
 //                done): part[c, slice] = sum over the lists of chunk c of
 //                act * W_down_t[i, slice]
 //   reduce_groups h = h + sum_c part[c]
-// Single calls (spffn_predict / spffn_forward at one token): w1_b1, w2_b1
+// Single calls (spffn_predict / spffn_forward at one token): w1x_b1, w2_b1
 // (logits and mask), up_b1 (activations of an index list), down_b1 (partials
 // over contiguous runs of the list), reduce_groups.
 // (s is the RMS scale; multiplying the dot product by it equals normalising
@@ -65,69 +65,88 @@ __device__ __forceinline__ float stage_vec(const float *__restrict__ x, int d, f
     return ss;
 }
 
-// Block-wide sum of one float per thread, same order in every block.
-__device__ __forceinline__ float block_sum(float v, float *red) {
-    v = wave_sum(v);
-    const int nw = blockDim.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float t = 0.0f;
-    for (int w = 0; w < nw; ++w) t += red[w];
-    return t;
-}
-
 // ---------------------------------------------------------------------------
-// predictor layer 1: one wave per row, 4 rows per block
+// predictor layer 1, activations in registers: RB rows per block, thread t
+// takes packets t + 256u of every row (coalesced), with the activation values
+// of those packets loaded once into registers; block-wide sums in a fixed
+// order.  Every block also sums h^2 over the whole vector in the same order,
+// so all of them use the same RMS scale.
 // ---------------------------------------------------------------------------
-template <int PF>
-__global__ __launch_bounds__(256) void w1_b1_kernel(WMat w1, int r, int d,
-                                                    const float *__restrict__ h, float eps,
-                                                    int normalize, const float *__restrict__ b1,
-                                                    float *__restrict__ hid,
-                                                    float *__restrict__ scale_out,
-                                                    const float *__restrict__ tvec, float t) {
+template <int PF, int RB>
+__global__ __launch_bounds__(256) void w1x_b1_kernel(WMat w1, int r, int d,
+                                                     const float *__restrict__ h, float eps,
+                                                     int normalize, const float *__restrict__ b1,
+                                                     float *__restrict__ hid,
+                                                     float *__restrict__ scale_out,
+                                                     const float *__restrict__ tvec, float t) {
     constexpr int E = PacketElems<PF>::value;
-    constexpr int U = 16;
-    extern __shared__ float xl[];
-    __shared__ float red[4];
+    constexpr int UB = E >= 8 ? 32 / E : 4;  // packets per thread per pass
+    __shared__ float s_red[4][RB + 1];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int row = blockIdx.x * 4 + wv;
-    const bool rv = row < r;
     const int NP = d / E;
-    const uint4 *rp = row_ptr<PF>(w1, rv ? row : 0, d);
-
-    uint4 raw[U];
+    const int r0 = blockIdx.x * RB;
+    const uint4 *q[RB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = u * 64 + lane;
-        raw[u] = (rv && p < NP) ? ld_stream(rp + p) : make_uint4(0, 0, 0, 0);
-    }
-    const float ss = block_sum(stage_vec<E>(h, d, xl), red);  // contains the barrier
-    const float s = normalize ? 1.0f / sqrtf(ss / (float)d + eps) : 1.0f;
-    // scale_out[0] = the RMS scale, scale_out[1] = the token's logit
-    // threshold (its own, or the layer's): the layer kernel reads both at once
-    if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) {
-        scale_out[0] = s;
-        scale_out[1] = tvec ? *tvec : t;
-    }
-
-    float acc[1] = {0.0f};
-    for (int pg = 0; pg < NP; pg += 64 * U) {
-        if (pg > 0) {
+    for (int k = 0; k < RB; ++k) q[k] = row_ptr<PF>(w1, min(r0 + k, r - 1), d);
+    float acc[RB], ss = 0.0f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = pg + u * 64 + lane;
-                raw[u] = (rv && p < NP) ? ld_stream(rp + p) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < RB; ++k) acc[k] = 0.0f;
+    for (int pb = 0; pb < NP; pb += 256 * UB) {
+        uint4 w[RB][UB];
+        float xv[UB][E];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const int p = pb + (int)threadIdx.x + 256 * u;
+            const int pc = p < NP ? p : NP - 1;
+#pragma unroll
+            for (int k = 0; k < RB; ++k) w[k][u] = ld_stream(q[k] + pc);
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const int p = pb + (int)threadIdx.x + 256 * u;
+            float unused;
+            load_packet_x<PF>(h, p < NP ? p : NP - 1, xv[u], unused);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            // packets past the end of the rows meet zero activations
+            if (pb + (int)threadIdx.x + 256 * u >= NP) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) xv[u][e] = 0.0f;
             }
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = pg + u * 64 + lane;
-            if (p < NP) packet_dot<PF, 1>(raw[u], 1.0f, xl, NP, p, nullptr, acc);
+            for (int e = 0; e < E; ++e) ss = fmaf(xv[u][e], xv[u][e], ss);
+#pragma unroll
+            for (int k = 0; k < RB; ++k) acc[k] = packet_dot_reg<PF>(w[k][u], 1.0f, xv[u], 0.0f, acc[k]);
         }
     }
-    const float v = wave_sum(acc[0]) * row_scale<PF>(w1, rv ? row : 0);
-    if (rv && lane == 0) hid[row] = fmaxf(fmaf(v, s, b1 ? b1[row] : 0.0f), 0.0f);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) acc[k] = wave_sum(acc[k]);
+    ss = wave_sum(ss);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) s_red[wv][k] = acc[k];
+        s_red[wv][RB] = ss;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x <= RB) {
+        const int k = threadIdx.x;
+        const float sst = ((s_red[0][RB] + s_red[1][RB]) + s_red[2][RB]) + s_red[3][RB];
+        const float s = normalize ? 1.0f / sqrtf(sst / (float)d + eps) : 1.0f;
+        if (k < RB) {
+            const int row = r0 + k;
+            if (row < r) {
+                const float tot = ((s_red[0][k] + s_red[1][k]) + s_red[2][k]) + s_red[3][k];
+                hid[row] = fmaxf(fmaf(tot * row_scale<PF>(w1, row), s, b1 ? b1[row] : 0.0f), 0.0f);
+            }
+        } else if (blockIdx.x == 0 && scale_out) {
+            // scale_out[0] = the RMS scale, scale_out[1] = the token's logit
+            // threshold (its own, or the layer's): the layer kernel reads both
+            scale_out[0] = s;
+            scale_out[1] = tvec ? *tvec : t;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -899,17 +918,17 @@ bool b1_fits(const Layer &L) {
 hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
                         float *scale_out, hipStream_t s, const float *tvec) {
     const spffn_layer_desc &D = L.desc;
-    const int blocks = (D.r + 3) / 4;
-    const size_t lds = (size_t)D.d * 4;
+    constexpr int RB = 4;
+    const int blocks = (D.r + RB - 1) / RB;
     if (D.p_dtype == SPFFN_F16)
-        w1_b1_kernel<kF16><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out, tvec, L.t);
+        w1x_b1_kernel<kF16, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
+                                                       hid, scale_out, tvec, L.t);
     else if (D.p_dtype == SPFFN_FP8_E4M3)
-        w1_b1_kernel<kFP8><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out, tvec, L.t);
+        w1x_b1_kernel<kFP8, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
+                                                       hid, scale_out, tvec, L.t);
     else
-        w1_b1_kernel<kF32><<<blocks, 256, lds, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid,
-                                                    scale_out, tvec, L.t);
+        w1x_b1_kernel<kF32, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
+                                                       hid, scale_out, tvec, L.t);
     return hipGetLastError();
 }
 
