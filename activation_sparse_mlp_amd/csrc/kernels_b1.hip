@@ -899,7 +899,11 @@ __global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer
         s_gmask = gm;
     }
     // every wave issues its slot loads after this barrier, so after the count
-    // was seen complete
+    // was seen complete.  The poll is relaxed on purpose: the slots are read
+    // with agent-scope loads, which see the writers' agent-scope stores once
+    // those have completed (each writer waits for that before its increment);
+    // an acquire fence here invalidates the cache once per workgroup and
+    // measured 45.5 against 38.6 us per launch at the 70B shape.
     __syncthreads();
     down_chunk<FMT, UR>(dn, slice, c, s_ready != 0, s_gmask);
 }
