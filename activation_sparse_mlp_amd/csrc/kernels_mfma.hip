@@ -629,10 +629,14 @@ __global__ __launch_bounds__(256) void bdown_kernel(BdArgs a) {
 constexpr int kBgWaves = 4;
 constexpr int kW1Splits = 8;  // K splits of predictor layer 1 (few rows, long K)
 constexpr int kBdChunks = 32;
-// The gathered gate/up products have few row tiles (one per 16 listed rows)
-// and a long K, so each tile gets more waves: as many as the 64 KB of staging
-// LDS allows (16 for one matrix, 8 for gate and up; half that at B > 8).
-constexpr int kGatherWaves = 16, kGatherWavesG = 8;
+// The gathered gate/up products have one row tile per 16 listed rows and a
+// long K, so each tile gets several waves, each a K range (half as many at
+// B > 8).  Gate and up: 8 waves (4 measured 3.5-9% slower at the 70B and 7B
+// shapes).  One matrix (ReLU): 8 waves; with the 40B-shaped stack's 40% union
+// at B = 8 (~830 tiles) 16 waves per tile took 119.3 us per layer, 8 waves
+// 114.0 and 4 waves 128.3 (16 had paid only while the union was ~200 tiles,
+// fewer than the CUs).
+constexpr int kGatherWaves = 8, kGatherWavesG = 8;
 // workgroups of a gather whose list comes from tile masks (two per CU)
 constexpr int kGatherMaxTiles = 512;
 
