@@ -1060,15 +1060,15 @@ int fused_groups(const Layer &L) {
 
 // Down-projection chunks: ranges of NG consecutive row groups, NG <= 32 (one
 // flag bit per group in the chunk counter; a chunk's slots fit the down
-// workgroup's LDS list), at least 128 chunks (192
-// for 4-bit rows) when there are that many groups: smaller chunks complete
-// sooner after their last group, more of them cost more partial sums.
-// Measured per step, 70B shape: 32 chunks 4.15 ms, 64 3.87, 96 3.86, 128
-// 3.83, 192 4.00, 256 4.27; 7B: 64 0.810, 128 0.802, 192 0.827; 175B 4-bit:
-// 64 8.21, 128 7.46, 192 7.32, 256 7.33.
+// workgroup's LDS list), at least 128 chunks when there are that many
+// groups: smaller chunks complete sooner after their last group, more of them
+// cost more partial sums.  Measured per step, 70B shape: 32 chunks 4.15 ms,
+// 64 3.87, 96 3.86, 128 3.83, 192 4.00, 256 4.27; 7B: 64 0.810, 128 0.802,
+// 192 0.827.  175B 4-bit, per layer on the stack calibrated layer by layer
+// (5.3% active): 96 chunks 57.96 us, 128 57.21, 192 58.44.
 int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
-    const int cmin = L.desc.w_dtype == SPFFN_Q4_0 ? 192 : 128;
+    const int cmin = 128;
     int c = (G + 31) / 32;  // at most 32 groups: one flag bit each in the counter
     if (c < cmin) c = cmin;
     if (c > G) c = G;
