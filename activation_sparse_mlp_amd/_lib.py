@@ -70,6 +70,7 @@ SIGNATURES = {
     "spffn_graph_launch": (_i32, [_vp, _vp]),
     "spffn_graph_destroy": (None, [_vp]),
     "spffn_profile": (_i32, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "spffn_profile_workspace_bytes": (_sz, [_vp]),
     "spffn_hot_first_order": (_i32, [_vp, _i32, _vp, _vp]),
     "spffn_permute_rows": (_i32, [_vp, _vp, _vp, _i32, _i64, _vp]),
     "spffn_q4_0_repack": (_i32, [_vp, _vp, _i32, _i32, _vp]),
@@ -515,15 +516,20 @@ class DecodeGraph:
             self.handle = None
 
 
-def profile(layer, x, counts=None):
-    """counts int32 [d_ffn] += tokens of x [N, d] with a positive pre-activation."""
+def profile(layer, x, counts=None, scratch=True):
+    """counts int32 [d_ffn] += tokens of x [N, d] with a positive pre-activation.
+    With scratch (the default) the library gets the workspace that lets fp16
+    rows run on the matrix cores; scratch=False keeps the vector kernels."""
     N = _tokens(x, layer.d)
     _size(counts, layer.d_ffn, "counts")
     x = _dev(x, torch.float32, "x")
     if counts is None:
         counts = torch.zeros(layer.d_ffn, dtype=torch.int32, device=x.device)
     _dev(counts, torch.int32, "counts", layer.d_ffn)
-    _check(load().spffn_profile(layer.handle, _ptr(x), N, _ptr(counts), None, 0, _stream()),
+    nb = int(load().spffn_profile_workspace_bytes(layer.handle)) if scratch else 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=x.device) if nb else None
+    _check(load().spffn_profile(layer.handle, _ptr(x), N, _ptr(counts),
+                                _ptr(ws) if ws is not None else None, nb, _stream()),
            "spffn_profile")
     return counts
 

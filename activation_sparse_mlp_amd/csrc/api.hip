@@ -762,17 +762,28 @@ extern "C" {
 
 spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, int32_t *counts,
                            void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!layer || !x || !counts) return fail(SPFFN_E_ARG, "profile: NULL pointer");
     if (N < 1) return fail(SPFFN_E_SHAPE, "profile: N=%d < 1", N);
     if (!aligned(x, 16) || !aligned(counts, 4)) return fail(SPFFN_E_ARG, "profile: misaligned");
     const Layer &L = layer->L;
+    const size_t half_bytes = (size_t)16 * L.desc.d * sizeof(_Float16);
+    if (ws && ws_bytes >= spffn_profile_workspace_bytes(layer) && aligned(ws, 256) &&
+        mfma_profile_fits(L)) {
+        _Float16 *hi = static_cast<_Float16 *>(ws);
+        _Float16 *lo = reinterpret_cast<_Float16 *>(static_cast<char *>(ws) + half_bytes);
+        SPFFN_HIP(launch_mfma_profile(L, x, N, counts, hi, lo, (hipStream_t)stream),
+                  "profile launch");
+        return SPFFN_OK;
+    }
     const WMat &wa = L.desc.kind != SPFFN_RELU ? L.gate : L.up;
     SPFFN_HIP(launch_gemv_count(L.desc.w_dtype, wa, L.desc.d_ffn, L.desc.d, x, N, L.desc.b_act,
                                 counts, (hipStream_t)stream),
               "profile launch");
     return SPFFN_OK;
+}
+
+size_t spffn_profile_workspace_bytes(const spffn_layer *layer) {
+    return layer ? (size_t)2 * 16 * layer->L.desc.d * sizeof(_Float16) : 0;
 }
 
 spffn_status spffn_hot_first_order(const int32_t *counts, int32_t n, int32_t *perm,

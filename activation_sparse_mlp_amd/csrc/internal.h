@@ -104,6 +104,11 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
                           const float *act, float *part, int chunks, hipStream_t s);
 // Batched path on the matrix cores (fp16 weights, 2 <= B <= 16).
 bool mfma_fits(const Layer &L, int B);
+// Activation profile (counts += tokens with a positive pre-activation) of
+// fp16 rows on the matrix cores; hi, lo: 16 * d halves each of scratch.
+bool mfma_profile_fits(const Layer &L);
+hipError_t launch_mfma_profile(const Layer &L, const float *x, int N, int32_t *counts,
+                               _Float16 *hi, _Float16 *lo, hipStream_t s);
 int mfma_down_chunks();
 int mfma_w1_splits();
 hipError_t launch_split_act(const float *x, int B, int K, float eps, bool normalize, float *n_out,

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void split_act_kernel(const float *__restrict_
 // below; blockIdx.y picks the range when K is split across workgroups),
 // reduced over the waves in a fixed order, then one of three epilogues.
 // ---------------------------------------------------------------------------
-enum { kEpiPartial = 0, kEpiMask = 1, kEpiAct = 2 };
+enum { kEpiPartial = 0, kEpiMask = 1, kEpiAct = 2, kEpiCount = 3 };
 
 struct BgArgs {
     const _Float16 *wa;  // [rows, K] (gate for ReGLU, else the one matrix)
@@ -154,6 +154,7 @@ struct BgArgs {
     int ld_act;
     const float *tsc;      // act: per-token scale of the products (raw input), or nullptr
     bool silu;             // act: SwiGLU (SiLU instead of ReLU on the gate)
+    int32_t *counts;       // count: [rows] += tokens with Z + bias > 0
 };
 
 template <int WV, int T, bool GATED, bool SPLIT2, int EPI>
@@ -361,6 +362,8 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                 if (a.logits) a.logits[(size_t)n * a.rows + rr] = l;
                 if (a.mask) a.mask[(size_t)n * a.rows + rr] = (uint8_t)mk;
                 if (mk) atomicOr(&s_any[16 * t + r], 1u);  // LDS
+            } else if constexpr (EPI == kEpiCount) {
+                if (za + (a.bias ? a.bias[rr] : 0.0f) > 0.0f) atomicAdd(&s_any[16 * t + r], 1u);
             } else {
                 const float sc = a.tsc ? a.tsc[n] : 1.0f;
                 float v = gate_act(fmaf(za, sc, a.bias ? a.bias[rr] : 0.0f), a.silu);
@@ -369,6 +372,13 @@ __global__ __launch_bounds__(64 * WV) void bgemv_kernel(BgArgs a) {
                 a.ahi[(size_t)n * a.ld_act + jj] = h;
                 a.alo[(size_t)n * a.ld_act + jj] = (_Float16)(v - (float)h);
             }
+        }
+        if constexpr (EPI == kEpiCount) {
+            // one thread per row adds the tile's count (launches of one
+            // profile call run in stream order, so plain updates suffice)
+            __syncthreads();
+            if ((int)threadIdx.x < 16 * T && j0 + (int)threadIdx.x < n_items)
+                a.counts[row_of(j0 + threadIdx.x)] += (int32_t)s_any[threadIdx.x];
         }
         if constexpr (EPI == kEpiMask) {
             __syncthreads();
@@ -685,6 +695,36 @@ static void launch_bg(const BgArgs &a, dim3 grid, hipStream_t s) {
     } else {
         bgemv_kernel<WV1, 1, GATED, false, EPI><<<grid, 64 * WV1, 0, s>>>(a);
     }
+}
+
+// Activation profile of fp16 rows on the matrix cores: tokens in groups of
+// 16, each split into packed fp16 halves (hi, lo: 16 * d halves each), then
+// one dense pass of the activated matrix with the count epilogue.
+bool mfma_profile_fits(const Layer &L) {
+    return L.desc.w_dtype == SPFFN_F16 && L.desc.d % (128 * kBgWaves) == 0;
+}
+
+hipError_t launch_mfma_profile(const Layer &L, const float *x, int N, int32_t *counts,
+                               _Float16 *hi, _Float16 *lo, hipStream_t s) {
+    const spffn_layer_desc &D = L.desc;
+    for (int b0 = 0; b0 < N; b0 += 16) {
+        const int nb = N - b0 < 16 ? N - b0 : 16;
+        split_act_kernel<<<dim3(nb, kSplitChunks), 256, 0, s>>>(x + (size_t)b0 * D.d, D.d, 0.0f,
+                                                                0, nullptr, hi, lo);
+        BgArgs a{};
+        a.wa = reinterpret_cast<const _Float16 *>((D.kind != SPFFN_RELU ? L.gate : L.up).data);
+        a.K = D.d;
+        a.rows = D.d_ffn;
+        a.xhi = hi;
+        a.xlo = lo;
+        a.B = nb;
+        a.bias = D.b_act;
+        a.counts = counts;
+        launch_bg<false, kEpiCount, kBgWaves, kBgWaves>(a, dim3((D.d_ffn + 15) / 16, 1), s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_mfma_predict(const Layer &L, const _Float16 *xhi, const _Float16 *xlo, int B,

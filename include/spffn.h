@@ -326,9 +326,18 @@ void spffn_graph_destroy(spffn_graph *graph);
 /* Activation profile over N tokens x [N, d] (N >= 1): counts[i] (device
  * int32 [d_ffn]) += the number of tokens with a positive pre-activation of
  * neuron i (W_gate for ReGLU, W_up for ReLU, plus bias).  Accumulates, so the
- * caller zeroes counts first.  Guide Step 1 "Offline Activation Profiler". */
+ * caller zeroes counts first.  Guide Step 1 "Offline Activation Profiler".
+ * ws (device, 256-byte aligned, caller-owned) is optional: with at least
+ * spffn_profile_workspace_bytes(layer) bytes, fp16 rows with d a multiple of
+ * 512 are profiled on the matrix cores (the tokens split into fp16 halves, as
+ * the batched decode does); otherwise, or with ws NULL, the vector kernels run.
+ * A count can then differ only for tokens whose pre-activation is within
+ * rounding of zero. */
 spffn_status spffn_profile(const spffn_layer *layer, const float *x, int32_t N, int32_t *counts,
                            void *ws, size_t ws_bytes, void *stream);
+
+/* Scratch bytes that let spffn_profile use the matrix cores (0 for NULL). */
+size_t spffn_profile_workspace_bytes(const spffn_layer *layer);
 
 /* Hot-first order of n neurons from their counts: perm[k] = the neuron of
  * rank k when sorted by count descending, ties by ascending index (a stable

@@ -240,6 +240,41 @@ def test_profile_counts():
     assert np.mean(got == ref) > 0.99
 
 
+_PROF_F16 = replace(LLAMA2_7B, d=1024, d_ffn=1000, r=64)      # fp16 rows, d a multiple of 512
+_PROF_RELU = replace(LLAMA2_7B, kind="relu", d=512, d_ffn=700, r=64)
+
+
+def _near_zero_tokens(L, X):
+    near = np.zeros(L["d_ffn"], np.int64)
+    for x in X:
+        z = oracle.preact(L, x)[0]
+        near += np.abs(z) < 1e-4
+    return near
+
+
+@pytest.mark.parametrize("cfg", [_PROF_F16, _PROF_RELU])
+@pytest.mark.parametrize("N", [1, 5, 13, 40])
+def test_profile_counts_matrix_cores(cfg, N):
+    """fp16 rows are profiled on the matrix cores when the library gets its
+    scratch (tokens in groups of 16: one or two halves per instruction, and a
+    ragged last group); counts against the oracle, and against the vector
+    kernels, within the tokens whose pre-activation is near zero."""
+    w = make_layer(cfg, 0, seed=16, n_cal=512)
+    G, L = gpu_layer(w), np_layer(w)
+    X = make_tokens(cfg.d, N, 1, seed=17)[:, 0, :]
+    assert spffn.load().spffn_profile_workspace_bytes(G.handle) == 64 * cfg.d
+    got = spffn.profile(G, X.to(DEV)).cpu().numpy()
+    vec = spffn.profile(G, X.to(DEV), scratch=False).cpu().numpy()
+    ref = oracle.profile(L, X.numpy())
+    near = _near_zero_tokens(L, X.numpy())
+    assert np.all(np.abs(got - ref) <= near)
+    assert np.all(np.abs(got - vec) <= near)
+    assert np.mean(got == ref) > 0.99
+    # counts accumulate across calls
+    twice = spffn.profile(G, X.to(DEV), counts=torch.from_numpy(got).to(DEV)).cpu().numpy()
+    assert np.array_equal(twice, 2 * got)
+
+
 @pytest.mark.parametrize("n", [1, 5, 1000, 28672])
 def test_hot_first_order_bit_exact(n):
     rng = np.random.default_rng(n)
