@@ -142,30 +142,42 @@ hipError_t launch_compact(const uint8_t *mask, int n, int32_t *idx, int32_t *cou
 
 // ---------------------------------------------------------------------------
 // hot-first order: rank_i = #{j : c_j > c_i} + #{j < i : c_j == c_i};
-// perm[rank_i] = i.  O(n^2) comparisons, tiled through LDS; load time only.
+// perm[rank_i] = i.  O(n^2) integer comparisons, load time only.  A block of
+// 16 waves ranks 64 neurons (one per lane): the counts pass through LDS in
+// tiles of 1024, each wave compares its lanes' neurons against 64 entries of
+// every tile (an LDS broadcast per entry), and the 16 partial ranks are added
+// at the end.  (One thread per neuron over the whole array left most SIMDs
+// idle: 0.81 ms at 28672 neurons.)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void hot_first_order_kernel(const int32_t *__restrict__ counts,
-                                                              int n, int32_t *__restrict__ perm) {
+__global__ __launch_bounds__(1024) void hot_first_order_kernel(const int32_t *__restrict__ counts,
+                                                               int n, int32_t *__restrict__ perm) {
     __shared__ int32_t tile[1024];
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ int32_t part[16][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int i = blockIdx.x * 64 + lane;
     const int ci = i < n ? counts[i] : 0;
     int rank = 0;
     for (int base = 0; base < n; base += 1024) {
         __syncthreads();
-        for (int t = threadIdx.x; t < 1024; t += blockDim.x)
-            tile[t] = base + t < n ? counts[base + t] : 0;
+        tile[threadIdx.x] = base + (int)threadIdx.x < n ? counts[base + threadIdx.x] : 0;
         __syncthreads();
-        const int lim = min(1024, n - base);
-        for (int t = 0; t < lim; ++t) {
+        const int t1 = min(wv * 64 + 64, n - base);
+        for (int t = wv * 64; t < t1; ++t) {
             const int cj = tile[t];
             rank += (cj > ci) | ((cj == ci) & (base + t < i));
         }
     }
-    if (i < n) perm[rank] = i;
+    part[wv][lane] = rank;
+    __syncthreads();
+    if (wv == 0 && i < n) {
+        int r = 0;
+        for (int w = 0; w < 16; ++w) r += part[w][lane];
+        perm[r] = i;
+    }
 }
 
 hipError_t launch_hot_first_order(const int32_t *counts, int n, int32_t *perm, hipStream_t s) {
-    hot_first_order_kernel<<<(n + 255) / 256, 256, 0, s>>>(counts, n, perm);
+    hot_first_order_kernel<<<(n + 63) / 64, 1024, 0, s>>>(counts, n, perm);
     return hipGetLastError();
 }
 
