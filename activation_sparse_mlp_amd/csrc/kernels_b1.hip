@@ -72,15 +72,14 @@ __device__ __forceinline__ float stage_vec(const float *__restrict__ x, int d, f
 // order.  Every block also sums h^2 over the whole vector in the same order,
 // so all of them use the same RMS scale.
 // ---------------------------------------------------------------------------
-template <int PF, int RB>
+template <int PF, int RB, int UB>
 __global__ __launch_bounds__(256) void w1x_b1_kernel(WMat w1, int r, int d,
                                                      const float *__restrict__ h, float eps,
                                                      int normalize, const float *__restrict__ b1,
                                                      float *__restrict__ hid,
                                                      float *__restrict__ scale_out,
                                                      const float *__restrict__ tvec, float t) {
-    constexpr int E = PacketElems<PF>::value;
-    constexpr int UB = E >= 8 ? 32 / E : 4;  // packets per thread per pass
+    constexpr int E = PacketElems<PF>::value;  // UB: packets per thread per pass
     __shared__ float s_red[4][RB + 1];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int NP = d / E;
@@ -919,20 +918,36 @@ bool b1_fits(const Layer &L) {
     return lds <= 56 * 1024 && (size_t)L.desc.r * 4 <= 56 * 1024;
 }
 
+// Packets per thread per pass: as many as one pass needs (a row of NP packets
+// over 256 threads), at most 32 activation values per thread (4 packets for
+// fp32 rows).
+template <int PF, int RB, int UBMAX>
+static void launch_w1x(const Layer &L, const float *h, float eps, bool normalize, float *hid,
+                       float *scale_out, hipStream_t s, const float *tvec) {
+    const spffn_layer_desc &D = L.desc;
+    const int blocks = (D.r + RB - 1) / RB;
+    const int NP = D.d / PacketElems<PF>::value;
+    const int ub = NP <= 256 ? 1 : NP <= 512 ? 2 : 4;
+    if (ub == 1 || UBMAX == 1)
+        w1x_b1_kernel<PF, RB, 1><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
+                                                        hid, scale_out, tvec, L.t);
+    else if (ub == 2 || UBMAX == 2)
+        w1x_b1_kernel<PF, RB, (UBMAX < 2 ? UBMAX : 2)><<<blocks, 256, 0, s>>>(
+            L.w1, D.r, D.d, h, eps, normalize, D.p_b1, hid, scale_out, tvec, L.t);
+    else
+        w1x_b1_kernel<PF, RB, UBMAX><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize,
+                                                            D.p_b1, hid, scale_out, tvec, L.t);
+}
+
 hipError_t launch_w1_b1(const Layer &L, const float *h, float eps, bool normalize, float *hid,
                         float *scale_out, hipStream_t s, const float *tvec) {
-    const spffn_layer_desc &D = L.desc;
     constexpr int RB = 4;
-    const int blocks = (D.r + RB - 1) / RB;
-    if (D.p_dtype == SPFFN_F16)
-        w1x_b1_kernel<kF16, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
-                                                       hid, scale_out, tvec, L.t);
-    else if (D.p_dtype == SPFFN_FP8_E4M3)
-        w1x_b1_kernel<kFP8, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
-                                                       hid, scale_out, tvec, L.t);
+    if (L.desc.p_dtype == SPFFN_F16)
+        launch_w1x<kF16, RB, 4>(L, h, eps, normalize, hid, scale_out, s, tvec);
+    else if (L.desc.p_dtype == SPFFN_FP8_E4M3)
+        launch_w1x<kFP8, RB, 2>(L, h, eps, normalize, hid, scale_out, s, tvec);
     else
-        w1x_b1_kernel<kF32, RB><<<blocks, 256, 0, s>>>(L.w1, D.r, D.d, h, eps, normalize, D.p_b1,
-                                                       hid, scale_out, tvec, L.t);
+        launch_w1x<kF32, RB, 4>(L, h, eps, normalize, hid, scale_out, s, tvec);
     return hipGetLastError();
 }
 
