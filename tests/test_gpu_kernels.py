@@ -275,7 +275,9 @@ def test_profile_counts_matrix_cores(cfg, N):
     assert np.array_equal(twice, 2 * got)
 
 
-@pytest.mark.parametrize("n", [1, 5, 1000, 28672])
+# sizes around the kernel's 64-neuron blocks and 1024-entry tiles, and the
+# full 70B width
+@pytest.mark.parametrize("n", [1, 5, 63, 64, 65, 1000, 1023, 1024, 1025, 28672])
 def test_hot_first_order_bit_exact(n):
     rng = np.random.default_rng(n)
     counts = rng.integers(0, 20, size=n).astype(np.int32)
