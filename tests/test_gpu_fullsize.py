@@ -4,8 +4,8 @@ layer by layer against the CPU oracle (teacher forced through the trace).
 Stacks are generated as the benchmark generates them (make_stack: every layer
 calibrated on the inputs it receives; 4096 calibration tokens; 256 profile
 tokens for the hot-first order; the benchmark's first token), and the deep
-stacks are checked at their first, second, middle and last layers.  Large
-batches are checked on sampled tokens."""
+stacks (7B, 40B, 70B, 175B) are checked at their first, second, middle and
+last layers.  Large batches are checked on sampled tokens."""
 import numpy as np
 import pytest
 import torch
@@ -113,6 +113,24 @@ def test_llama2_70b_benchmarked_stack_deep_layers():
 
 def test_llama2_7b_decode_b1():
     _decode_check(LLAMA2_7B, 1, 2, hot_first=False)
+
+
+@pytest.mark.timeout(600)
+def test_llama2_7b_benchmarked_stack_deep_layers():
+    """The whole 32-layer 7B-shaped stack the benchmark times, one traced step,
+    checked at layers 0, 1, 16 and 31."""
+    acts = _decode_check(LLAMA2_7B, 1, LLAMA2_7B.layers, hot_first=False,
+                         layers_checked=[0, 1, 16, 31])
+    assert abs(acts.mean() - LLAMA2_7B.mean_activity) < 0.02
+
+
+@pytest.mark.timeout(600)
+def test_falcon_40b_benchmarked_stack_deep_layers():
+    """The whole 60-layer 40B-shaped ReLU stack the benchmark times, one traced
+    step, checked at layers 0, 1, 30 and 59."""
+    acts = _decode_check(FALCON_40B, 1, FALCON_40B.layers, hot_first=False,
+                         layers_checked=[0, 1, 30, 59])
+    assert abs(acts.mean() - FALCON_40B.mean_activity) < 0.02
 
 
 def test_falcon_40b_decode_b1():
