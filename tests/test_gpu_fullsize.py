@@ -148,6 +148,23 @@ def test_falcon_40b_decode_b8():
     _decode_check(FALCON_40B, 8, 1, hot_first=False, tokens_checked=[0, 7])
 
 
+@pytest.mark.timeout(600)
+def test_llama2_70b_benchmarked_stack_deep_layers_b16():
+    """The 80-layer stack at B = 16 (the matrix-core path the benchmark times),
+    one traced step, checked at layers 0, 40 and 79 on the first and last
+    tokens."""
+    _decode_check(LLAMA2_70B, 16, LLAMA2_70B.layers, hot_first=True, tokens_checked=[0, 15],
+                  layers_checked=[0, 40, 79])
+
+
+@pytest.mark.timeout(600)
+def test_falcon_40b_benchmarked_stack_deep_layers_b8():
+    """The 60-layer ReLU stack at B = 8, one traced step, checked at layers 0,
+    30 and 59 on the first and last tokens."""
+    _decode_check(FALCON_40B, 8, FALCON_40B.layers, hot_first=False, tokens_checked=[0, 7],
+                  layers_checked=[0, 30, 59])
+
+
 def test_opt_175b_q4_0_decode_b1():
     _decode_check(OPT_175B_Q4, 1, 1, hot_first=False)
 
