@@ -737,9 +737,16 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
     constexpr int E = PacketElems<FMT>::value;
     constexpr int SPT = kDownListMaxSlots / 256;  // slots per thread
     constexpr int RP = red_pitch<E>();
-    __shared__ float red[4 * 64 * E <= kDownListMaxSlots ? 1 : 64 * RP];
-    __shared__ int s_i[kDownListMaxSlots];
-    __shared__ float s_a[kDownListMaxSlots];
+    // The chunk's compacted list (neurons, then activations) in one array,
+    // which also holds the four waves' column sums at the end when they fit
+    // (fp32 and fp16 packets: two barriers instead of a chain of four, the
+    // same order of additions; 70B-shaped layer 46.7 -> 46.5 us, 7B-shaped
+    // 24.2 -> 23.9 us); wider packets sum through `red`.
+    constexpr bool WREG = 4 * 64 * E <= 2 * kDownListMaxSlots;
+    __shared__ float red[WREG ? 1 : 64 * RP];
+    __shared__ int s_list[2 * kDownListMaxSlots];
+    int *const s_i = s_list;
+    float *const s_a = reinterpret_cast<float *>(s_list + kDownListMaxSlots);
     __shared__ int s_wc[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int NP = a.d / E;
@@ -834,11 +841,11 @@ __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slic
     }
 
     packet_axpy_finish<FMT>(acc, corr);
-    if constexpr (4 * 64 * E <= kDownListMaxSlots) {
+    if constexpr (WREG) {
         // every wave parks its sums in a region of its own (the list's LDS,
         // free once all waves are past their loads), then the four regions
-        // are added in wave order: two barriers instead of a chain of four
-        float *wr = reinterpret_cast<float *>(s_i);
+        // are added in wave order
+        float *wr = reinterpret_cast<float *>(s_list);
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < E; ++e) wr[(wv * 64 + lane) * E + e] = acc[e];
