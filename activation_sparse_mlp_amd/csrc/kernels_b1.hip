@@ -495,13 +495,53 @@ struct FusedArgs {
     bool adapt;           // host only: the token's threshold is at scale[1], not t
 };
 
+// Row groups of the layer kernel: a group of 4 RW P rows reads its W2 rows in
+// P passes of RW rows per wave (each pass's rows are requested once the
+// previous pass's are multiplied), so a group costs the registers of one pass.
+// Gated rows (ReGLU, SwiGLU): 8-row groups in one pass.  Small groups keep the
+// kernel at 4-5 resident workgroups per CU and let the hardware hand new
+// groups to CUs whose groups had few active rows, which balances the gather
+// phase better than larger groups.
+constexpr int kFusedRW = 2, kPassesGated = 1;
+// (At the 70B shape only 28-row groups in 7 passes, 1024 groups, measured
+// faster, by 0.6%; 12, 16, 24 and 32 rows in one to eight passes were 0.5-2.3%
+// slower, and at the 7B shape 12-row groups equal, 16 and 28 rows slower.)
+// Non-gated rows gather one matrix per active row, so a group's gather is half
+// as long and larger groups spread the W2 phase better: 32 rows in 8 passes of
+// one row per wave, 1024 groups at the 40B shape.  Per layer of a 40B-shaped
+// ReLU decode step (us): 12 rows in one pass 41.4, 12 rows as 3 x 4 41.6, 24
+// rows as 2 x 12 41.6, 32 rows as 4 x 8 40.4, 32 rows as 8 x 4 40.3 (one
+// pass: 8 rows 2.652 ms per step, 12 rows 2.574, 16 rows 2.695).
+constexpr int kFusedRWNonGated = 1, kPassesNonGated = 8;
+// 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
+// row reads the whole fp32 activation vector (and its block sums), so their
+// groups are large: 48 rows in 12 passes of one row per wave, which makes a
+// 175B-shaped layer 1024 groups, four per CU in one round.  Per layer of a
+// 175B-shaped decode step (us): 20 rows in one pass 56.4; 40 rows as 2 x 20
+// 55.0, 60 rows as 3 x 20 55.4; 48 rows as 3 x 16 53.9, 4 x 12 53.2, 6 x 8
+// 53.6, 12 x 4 52.1; one row per wave per pass for 40, 44, 56, 64 rows 54.0,
+// 54.2, 53.4, 53.8.
+constexpr int kFusedRWQ4 = 1, kPassesQ4 = 12;
+static_assert(4 * kFusedRW * kPassesGated <= 64 && 4 * kFusedRWQ4 * kPassesQ4 <= 64 &&
+                  4 * kFusedRWNonGated * kPassesNonGated <= 64,
+              "a row group's list slots are written by its first wave");
+
+template <int FMT, bool GATED> constexpr int fused_rw() {
+    return FMT == kQ4 ? kFusedRWQ4 : GATED ? kFusedRW : kFusedRWNonGated;
+}
+template <int FMT, bool GATED> constexpr int w2_passes() {
+    return FMT == kQ4 ? kPassesQ4 : GATED ? kPassesGated : kPassesNonGated;
+}
+
 template <int PF, int FMT, bool GATED, int RW, int UA, bool ADAPT>
 __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
-    constexpr int RB = 4 * RW;     // rows per row group (one group per workgroup)
+    constexpr int NPS = w2_passes<FMT, GATED>();  // W2 passes of RBP rows
+    constexpr int RBP = 4 * RW;
+    constexpr int RB = RBP * NPS;  // rows per row group (one group per workgroup)
     constexpr int PL = PF == kFP8 ? 1 : 2;  // W2 packets per lane per row (one pass)
-    __shared__ uint32_t s_bits[4];
+    __shared__ uint32_t s_bits[NPS][4];
     __shared__ float s_bias[RB];   // bias of every row of the group, by local index
     __shared__ float s_part[RB][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -536,12 +576,13 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         float unused;
         load_packet_x<PF>(a.hid, p < NPr ? p : NPr - 1, hv[u], unused);
     }
-    float b2v, rsv;
-    {
-        const int row = g + G * (wv + 4 * (lane < RW ? lane : 0));
+    float b2v[NPS], rsv[NPS];
+#pragma unroll
+    for (int ps = 0; ps < NPS; ++ps) {
+        const int row = g + G * (ps * RBP + wv + 4 * (lane < RW ? lane : 0));
         const int rr = row < a.d_ffn ? row : a.d_ffn - 1;
-        b2v = a.b2[rr];
-        rsv = row_scale<PF>(a.w2, rr);  // 1 except for fp8 predictor rows
+        b2v[ps] = a.b2[rr];
+        rsv[ps] = row_scale<PF>(a.w2, rr);  // 1 except for fp8 predictor rows
     }
     if ((int)threadIdx.x < RB) {
         const int row = g + G * (int)threadIdx.x;
@@ -561,43 +602,68 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         thr = a.t;
     }
 
-    // logits, threshold, mask
-    uint32_t bits = 0;
+    // logits, threshold, mask (pass ps: rows of local index ps * RBP + wv + 4q;
+    // the next pass's rows are requested once this pass's are multiplied)
+    uint32_t bits[NPS];
+#pragma unroll
+    for (int ps = 0; ps < NPS; ++ps) {
+    bits[ps] = 0;
+    if (ps > 0) {
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+            const int row = g + G * (ps * RBP + wv + 4 * q);
+            const bool rv = row < a.d_ffn && row >= a.kd;
+            const int rr = rv ? row : a.d_ffn - 1;
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int p = u * 64 + lane;
+                const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
+                rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
         float acc = 0.0f;
 #pragma unroll
         for (int u = 0; u < PL; ++u)
             if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
-        const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv), q));
+        const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[ps]), q));
         const float v = wave_sum(acc) * rq;
-        const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v), q));
-        const int row = g + G * (wv + 4 * q);
+        const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v[ps]), q));
+        const int row = g + G * (ps * RBP + wv + 4 * q);
         if (row < a.d_ffn) {
             const bool pre = row < a.kd;  // always-active prefix
             const float l = pre ? __builtin_inff() : v + bq;
             const bool m = pre || l > thr;
-            bits |= (uint32_t)m << q;
+            bits[ps] |= (uint32_t)m << q;
             if (lane == 0) {
                 if (a.logits) a.logits[row] = l;
                 a.mask[row] = (uint8_t)m;
             }
         }
     }
-    // the group's active rows as one mask over the local index k = wv + 4q
-    // (ascending k is ascending row g + G*k), built by every thread from the
-    // four waves' bits
-    if (lane == 0) s_bits[wv] = bits;
+    }
+    // the group's active rows as one mask over the local index
+    // k = ps * RBP + wv + 4q (ascending k is ascending row g + G*k), built by
+    // every thread from the four waves' bits
+    if (lane == 0) {
+#pragma unroll
+        for (int ps = 0; ps < NPS; ++ps) s_bits[ps][wv] = bits[ps];
+    }
     __syncthreads();
-    uint32_t act_mask = 0;
-    {
-        const uint32_t b0 = s_bits[0], b1 = s_bits[1], b2 = s_bits[2], b3 = s_bits[3];
+    unsigned long long act_mask = 0;
+#pragma unroll
+    for (int ps = 0; ps < NPS; ++ps) {
+        const unsigned long long b0 = s_bits[ps][0], b1 = s_bits[ps][1], b2 = s_bits[ps][2],
+                                 b3 = s_bits[ps][3];
+        const int o = ps * RBP;
 #pragma unroll
         for (int q = 0; q < RW; ++q)
-            act_mask |= (((b0 >> q) & 1u) << (4 * q)) | (((b1 >> q) & 1u) << (4 * q + 1)) |
-                        (((b2 >> q) & 1u) << (4 * q + 2)) | (((b3 >> q) & 1u) << (4 * q + 3));
+            act_mask |= (((b0 >> q) & 1ull) << (o + 4 * q)) | (((b1 >> q) & 1ull) << (o + 4 * q + 1)) |
+                        (((b2 >> q) & 1ull) << (o + 4 * q + 2)) | (((b3 >> q) & 1ull) << (o + 4 * q + 3));
     }
-    const int n_act = __popc(act_mask);
+    const int n_act = __popcll(act_mask);
 
     // activations of the listed rows: the four waves share each row, lane
     // (wv, lane) always takes packets wv*64 + lane + 256u, so its activation
@@ -606,9 +672,9 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     // Packets past the end of a row load a clamped (valid) packet and meet
     // zero activation values, so every load is unconditional.
     float xv[UA][E], xs[UA];
-    uint32_t pending = act_mask;
+    unsigned long long pending = act_mask;
     for (int k = 0; k < n_act; ++k) {
-        const int kl = __ffs(pending) - 1;  // local index of the k-th active row
+        const int kl = __ffsll(pending) - 1;  // local index of the k-th active row
         pending &= pending - 1;
         const int i = g + G * kl;
         uint4 ra[UA], ru[UA];
@@ -682,9 +748,9 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
                 vu += s_part[k][w][1];
             }
             // local index of the k-th active row
-            uint32_t m = act_mask;
+            unsigned long long m = act_mask;
             for (int j = 0; j < k; ++j) m &= m - 1;
-            const int kl = __ffs(m) - 1;
+            const int kl = __ffsll(m) - 1;
             v = gate_act(fmaf(vz, s, s_bias[kl]), a.silu);
             if constexpr (GATED) v *= vu * s;
             row = g + G * kl;
@@ -729,7 +795,7 @@ struct DownListArgs {
     int32_t *giveups;      // device count of workgroups that gave up waiting
 };
 
-constexpr int kDownListMaxSlots = 64 * 20;  // groups per chunk <= 32, rows per group <= 20
+constexpr int kDownListMaxSlots = 64 * 20;  // list slots of one chunk's groups
 
 template <int FMT, int UR>
 __device__ __forceinline__ void down_chunk(const DownListArgs &a, const int slice, const int c,
@@ -1056,34 +1122,10 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-// Row groups of the layer kernel: 8 rows per workgroup for gated rows (two
-// W2 rows per wave).  Small groups keep the kernel at 4-5 resident workgroups per CU and
-// let the hardware hand new groups to CUs whose groups had few active rows,
-// which balances the gather phase better than larger groups.
-constexpr int kFusedRW = 2;
-// Non-gated rows gather one matrix per active row, so a group's gather is half
-// as long and larger groups (12 rows) spread the W2 phase better (measured at
-// the 40B-shaped ReLU stack: 8 rows 2.652 ms per step, 12 rows 2.574, 16
-// rows 2.695; at the gated 7B and 70B shapes 8 rows stay best).
-constexpr int kFusedRWNonGated = 3;
-// 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
-// row still reads the whole fp32 activation vector (and its block sums), so
-// their groups are larger (20 rows) to spread that read over more active rows
-// (measured at the 175B-shaped layer: 8 rows 55.5 us, 12 rows 51.4, 16 rows
-// 50.4-51.2, 20 rows 48.0-48.7, 24 rows 55.2, 28 rows 49.7, 32 rows 52.4).
-constexpr int kFusedRWQ4 = 5;
-static_assert(4 * kFusedRW * 32 <= kDownListMaxSlots && 4 * kFusedRWQ4 * 32 <= kDownListMaxSlots &&
-                  4 * kFusedRWNonGated * 32 <= kDownListMaxSlots,
-              "a down-projection chunk must hold its groups' list slots");
-
-template <int FMT, bool GATED> constexpr int fused_rw() {
-    return FMT == kQ4 ? kFusedRWQ4 : GATED ? kFusedRW : kFusedRWNonGated;
-}
-
 int fused_rows_per_group(const Layer &L) {
-    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4
-                : L.desc.kind != SPFFN_RELU   ? kFusedRW
-                                              : kFusedRWNonGated);
+    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4 * kPassesQ4
+                : L.desc.kind != SPFFN_RELU   ? kFusedRW * kPassesGated
+                                              : kFusedRWNonGated * kPassesNonGated);
 }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
@@ -1100,8 +1142,11 @@ int fused_groups(const Layer &L) {
 // (5.3% active): 96 chunks 57.96 us, 128 57.21, 192 58.44.
 int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
+    // at most 32 groups (one flag bit each in the counter) whose list slots
+    // fit the down workgroup's LDS list
+    const int ngmax = std::min(32, kDownListMaxSlots / fused_rows_per_group(L));
     const int cmin = 128;
-    int c = (G + 31) / 32;  // at most 32 groups: one flag bit each in the counter
+    int c = (G + ngmax - 1) / ngmax;
     if (c < cmin) c = cmin;
     if (c > G) c = G;
     return (G + c - 1) / c;
