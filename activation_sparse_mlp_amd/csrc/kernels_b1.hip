@@ -1215,7 +1215,9 @@ int fused_groups(const Layer &L) {
 // cost more partial sums.  Measured per step, 70B shape: 32 chunks 4.15 ms,
 // 64 3.87, 96 3.86, 128 3.83, 192 4.00, 256 4.27; 7B: 64 0.810, 128 0.802,
 // 192 0.827.  175B 4-bit, per layer on the stack calibrated layer by layer
-// (5.3% active): 96 chunks 57.96 us, 128 57.21, 192 58.44.
+// (5.3% active): 96 chunks 57.96 us, 128 57.21, 192 58.44 with 20-row groups;
+// 64 chunks 54.2, 96 53.1, 128 51.9, 192 52.6 with 48-row groups.  40B ReLU
+// with 32-row groups: 64 chunks 39.8, 96 39.5, 128 39.35, 192 41.0.
 int fused_per_chunk(const Layer &L) {
     const int G = fused_groups(L);
     // at most 32 groups (one flag bit each in the counter) whose list slots
