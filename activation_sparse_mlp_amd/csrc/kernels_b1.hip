@@ -607,42 +607,42 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     uint32_t bits[NPS];
 #pragma unroll
     for (int ps = 0; ps < NPS; ++ps) {
-    bits[ps] = 0;
-    if (ps > 0) {
+        bits[ps] = 0;
+        if (ps > 0) {
+#pragma unroll
+            for (int q = 0; q < RW; ++q) {
+                const int row = g + G * (ps * RBP + wv + 4 * q);
+                const bool rv = row < a.d_ffn && row >= a.kd;
+                const int rr = rv ? row : a.d_ffn - 1;
+#pragma unroll
+                for (int u = 0; u < PL; ++u) {
+                    const int p = u * 64 + lane;
+                    const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
+                    rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
 #pragma unroll
         for (int q = 0; q < RW; ++q) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < PL; ++u)
+                if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
+            const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[ps]), q));
+            const float v = wave_sum(acc) * rq;
+            const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v[ps]), q));
             const int row = g + G * (ps * RBP + wv + 4 * q);
-            const bool rv = row < a.d_ffn && row >= a.kd;
-            const int rr = rv ? row : a.d_ffn - 1;
-#pragma unroll
-            for (int u = 0; u < PL; ++u) {
-                const int p = u * 64 + lane;
-                const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
-                rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
+            if (row < a.d_ffn) {
+                const bool pre = row < a.kd;  // always-active prefix
+                const float l = pre ? __builtin_inff() : v + bq;
+                const bool m = pre || l > thr;
+                bits[ps] |= (uint32_t)m << q;
+                if (lane == 0) {
+                    if (a.logits) a.logits[row] = l;
+                    a.mask[row] = (uint8_t)m;
+                }
             }
         }
-    }
-#pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int u = 0; u < PL; ++u)
-            if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
-        const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[ps]), q));
-        const float v = wave_sum(acc) * rq;
-        const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v[ps]), q));
-        const int row = g + G * (ps * RBP + wv + 4 * q);
-        if (row < a.d_ffn) {
-            const bool pre = row < a.kd;  // always-active prefix
-            const float l = pre ? __builtin_inff() : v + bq;
-            const bool m = pre || l > thr;
-            bits[ps] |= (uint32_t)m << q;
-            if (lane == 0) {
-                if (a.logits) a.logits[row] = l;
-                a.mask[row] = (uint8_t)m;
-            }
-        }
-    }
     }
     // the group's active rows as one mask over the local index
     // k = ps * RBP + wv + 4q (ascending k is ascending row g + G*k), built by
