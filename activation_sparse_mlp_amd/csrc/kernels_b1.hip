@@ -489,100 +489,98 @@ struct FusedArgs {
     uint8_t *mask;        // [d_ffn]
     int32_t *lst_i;       // [G*RB]
     float *lst_a;         // [G*RB]
+    int passes;           // W2 passes of 4 rows per row group (fused_passes)
     int per_chunk;        // NG: consecutive groups per down-projection chunk
     int32_t *done;        // [C * kDoneStride] per chunk, 64 bits: groups published (low
                           // word), groups with active rows (high word); zero at launch
     bool adapt;           // host only: the token's threshold is at scale[1], not t
 };
 
-// Row groups of the layer kernel: a group of 4 RW P rows reads its W2 rows in
-// P passes of RW rows per wave (each pass's rows are requested once the
-// previous pass's are multiplied), so a group costs the registers of one pass.
-// Gated rows (ReGLU, SwiGLU): 8-row groups in one pass.  Small groups keep the
-// kernel at 4-5 resident workgroups per CU and let the hardware hand new
-// groups to CUs whose groups had few active rows, which balances the gather
-// phase better than larger groups.
-constexpr int kFusedRW = 2, kPassesGated = 1;
-// (At the 70B shape only 28-row groups in 7 passes, 1024 groups, measured
-// faster, by 0.6%; 12, 16, 24 and 32 rows in one to eight passes were 0.5-2.3%
-// slower, and at the 7B shape 12-row groups equal, 16 and 28 rows slower.)
-// Non-gated rows gather one matrix per active row, so a group's gather is half
-// as long and larger groups spread the W2 phase better: 32 rows in 8 passes of
-// one row per wave, 1024 groups at the 40B shape.  Per layer of a 40B-shaped
-// ReLU decode step (us): 12 rows in one pass 41.4, 12 rows as 3 x 4 41.6, 24
-// rows as 2 x 12 41.6, 32 rows as 4 x 8 40.4, 32 rows as 8 x 4 40.3 (one
-// pass: 8 rows 2.652 ms per step, 12 rows 2.574, 16 rows 2.695).
-constexpr int kFusedRWNonGated = 1, kPassesNonGated = 8;
-// 4-bit rows are 4.5x smaller than fp16 ones while every group with an active
-// row reads the whole fp32 activation vector (and its block sums), so their
-// groups are large: 48 rows in 12 passes of one row per wave, which makes a
-// 175B-shaped layer 1024 groups, four per CU in one round.  Per layer of a
-// 175B-shaped decode step (us): 20 rows in one pass 56.4; 40 rows as 2 x 20
-// 55.0, 60 rows as 3 x 20 55.4; 48 rows as 3 x 16 53.9, 4 x 12 53.2, 6 x 8
-// 53.6, 12 x 4 52.1; one row per wave per pass for 40, 44, 56, 64 rows 54.0,
-// 54.2, 53.4, 53.8.
-constexpr int kFusedRWQ4 = 1, kPassesQ4 = 12;
-static_assert(4 * kFusedRW * kPassesGated <= 64 && 4 * kFusedRWQ4 * kPassesQ4 <= 64 &&
-                  4 * kFusedRWNonGated * kPassesNonGated <= 64,
-              "a row group's list slots are written by its first wave");
+// Row groups of the layer kernel.  A group's W2 rows are read in P passes of
+// one row per wave (4 rows a pass; each pass's rows are requested once the
+// previous pass's are multiplied), so a group costs the registers of one pass
+// whatever its size.  P is chosen per layer (fused_passes) so that the layer
+// has about kTargetGroups row groups -- four per CU of the 256 CUs: one round
+// of resident workgroups, with a slot per CU left to the down workgroups --
+// and a group at most 64 rows (its list slots are written by its first wave).
+// Found by sweeping fixed group sizes per layer of a decode step (us), against
+// the best one-pass groups: 175B-shaped 4-bit rows, 48 rows (12 passes) 52.1
+// against 20 rows 56.4 (one-row passes for 40, 44, 56, 64 rows 54.0, 54.2,
+// 53.4, 53.8; 48 rows in passes of 16, 12 or 8 rows 53.9, 53.2, 53.6);
+// 40B-shaped ReLU, 32 rows (8 passes) 40.3 against 12 rows 41.4 (24 rows in
+// passes of 12: 41.6; 32 rows in passes of 8: 40.4); 70B-shaped ReGLU, 28
+// rows (7 passes) 46.1 against 8 rows 46.4 (12, 16, 24 and 32 rows 0.5-2.3%
+// slower); 7B-shaped ReGLU, 12 rows (3 passes) 23.87 against 8 rows 23.87 (16
+// and 28 rows slower).  The per-layer pass count against those fixed shapes
+// per kind (whole decode steps on one box, ms): 70B 3.629 vs 3.681, 40B 2.333
+// vs 2.336, 7B 0.781 vs 0.775, 175B 5.123 vs 5.099.
+constexpr int kTargetGroups = 1024;
+constexpr int kMaxGroupRows = 64;
+// Rows per wave in a pass: one, except gated rows of at most 4096 columns
+// (UA <= 2, the 7B shape), whose small layers read two rows per wave in one
+// pass -- both rows in flight together, 8-row groups: 7B-shaped step 0.770 ms
+// against 0.785 for 12-row groups in three one-row passes and 0.783 for
+// 8-row groups in two.
+template <bool GATED, int UA> constexpr int pass_rows_per_wave() { return GATED && UA <= 2 ? 2 : 1; }
+// (The one-pass case must stay a compile-time constant: with the pass count
+// read from the arguments the 7B-shaped step took 0.785 ms against 0.772.)
 
-template <int FMT, bool GATED> constexpr int fused_rw() {
-    return FMT == kQ4 ? kFusedRWQ4 : GATED ? kFusedRW : kFusedRWNonGated;
-}
-template <int FMT, bool GATED> constexpr int w2_passes() {
-    return FMT == kQ4 ? kPassesQ4 : GATED ? kPassesGated : kPassesNonGated;
-}
-
-template <int PF, int FMT, bool GATED, int RW, int UA, bool ADAPT>
+template <int PF, int FMT, bool GATED, int UA, bool ADAPT>
 __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
-    constexpr int NPS = w2_passes<FMT, GATED>();  // W2 passes of RBP rows
-    constexpr int RBP = 4 * RW;
-    constexpr int RB = RBP * NPS;  // rows per row group (one group per workgroup)
     constexpr int PL = PF == kFP8 ? 1 : 2;  // W2 packets per lane per row (one pass)
-    __shared__ uint32_t s_bits[NPS][4];
-    __shared__ float s_bias[RB];   // bias of every row of the group, by local index
-    __shared__ float s_part[RB][4][2];
+    constexpr int RW = pass_rows_per_wave<GATED, UA>();
+    constexpr int RBP = 4 * RW;  // rows per pass
+    constexpr int RBMAX = RW == 2 ? RBP : kMaxGroupRows;  // rows per group at most
+    __shared__ uint32_t s_bits[4];
+    __shared__ float s_bias[RBMAX];  // bias of every row of the group, by local index
+    __shared__ float s_part[RBMAX][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int G = a.groups;
+    // W2 passes; row k = RBP ps + 4q + wv of the group in pass ps (always one
+    // pass with two rows per wave)
+    const int NPS = RW == 2 ? 1 : a.passes;
+    const int RB = RBP * NPS;  // rows per row group (one group per workgroup)
     const int NPr = a.r / EP, NPd = a.d / E;
 
-    // Everything the W2 phase needs is requested up front, straight into
-    // registers: the wave's W2 rows g + G*(wv + 4q), the hid values of the
-    // lane's two packets, the rows' b2 entries (lane q holds row q's) and the
-    // bias of each of the group's rows (into LDS).  Addresses are clamped into
-    // range and out-of-range values discarded, so the loads carry no branches.
-    // Rows of the always-active prefix are not scored: their loads are
-    // redirected to one fixed row (the last), so that no W2 row of the prefix
-    // is read from memory while every load stays unconditional.
+    // One pass's W2 operands of this wave, straight into registers: the rows
+    // g + G*(RBP ps + 4q + wv), q < RW, and their b2 entries and row scales
+    // (lane q holds row q's).  Addresses are clamped into range and
+    // out-of-range values discarded, so the loads carry no branches.  Rows of
+    // the always-active prefix are not scored: their loads are redirected to
+    // one fixed row (the last), so that no W2 row of the prefix is read from
+    // memory while every load stays unconditional.
     uint4 rc[RW][PL];
+    float b2v, rsv;
+    auto load_pass = [&](const int ps) {
 #pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        const int row = g + G * (wv + 4 * q);
-        const bool rv = row < a.d_ffn && row >= a.kd;
-        const int rr = rv ? row : a.d_ffn - 1;
+        for (int q = 0; q < RW; ++q) {
+            const int row = g + G * (RBP * ps + 4 * q + wv);
+            const bool rv = row < a.d_ffn && row >= a.kd;
+            const int rr = rv ? row : a.d_ffn - 1;
 #pragma unroll
-        for (int u = 0; u < PL; ++u) {
-            const int p = u * 64 + lane;
-            const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
-            rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < PL; ++u) {
+                const int p = u * 64 + lane;
+                const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
+                rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
+            }
         }
-    }
+        const int row = g + G * (RBP * ps + 4 * (lane < RW ? lane : 0) + wv);
+        const int rb = row < a.d_ffn ? row : a.d_ffn - 1;
+        b2v = a.b2[rb];
+        rsv = row_scale<PF>(a.w2, rb);  // 1 except for fp8 predictor rows
+    };
+    // Everything the first pass needs is requested up front: its W2 rows, the
+    // hid values of the lane's two packets, and the bias of each of the
+    // group's rows (into LDS).
+    load_pass(0);
     float hv[PL][EP];
 #pragma unroll
     for (int u = 0; u < PL; ++u) {
         const int p = u * 64 + lane;
         float unused;
         load_packet_x<PF>(a.hid, p < NPr ? p : NPr - 1, hv[u], unused);
-    }
-    float b2v[NPS], rsv[NPS];
-#pragma unroll
-    for (int ps = 0; ps < NPS; ++ps) {
-        const int row = g + G * (ps * RBP + wv + 4 * (lane < RW ? lane : 0));
-        const int rr = row < a.d_ffn ? row : a.d_ffn - 1;
-        b2v[ps] = a.b2[rr];
-        rsv[ps] = row_scale<PF>(a.w2, rr);  // 1 except for fp8 predictor rows
     }
     if ((int)threadIdx.x < RB) {
         const int row = g + G * (int)threadIdx.x;
@@ -602,66 +600,53 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
         thr = a.t;
     }
 
-    // logits, threshold, mask (pass ps: rows of local index ps * RBP + wv + 4q;
-    // the next pass's rows are requested once this pass's are multiplied)
-    uint32_t bits[NPS];
-#pragma unroll
-    for (int ps = 0; ps < NPS; ++ps) {
-        bits[ps] = 0;
-        if (ps > 0) {
-#pragma unroll
-            for (int q = 0; q < RW; ++q) {
-                const int row = g + G * (ps * RBP + wv + 4 * q);
-                const bool rv = row < a.d_ffn && row >= a.kd;
-                const int rr = rv ? row : a.d_ffn - 1;
-#pragma unroll
-                for (int u = 0; u < PL; ++u) {
-                    const int p = u * 64 + lane;
-                    const uint4 v = ld_stream(row_ptr<PF>(a.w2, rr, a.r) + (p < NPr ? p : NPr - 1));
-                    rc[q][u] = (rv && p < NPr) ? v : make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
+    // logits, threshold, mask; bit RW ps + q of `bits` is the wave's row q of
+    // pass ps (kept in a register: an LDS write of each pass's bits in the
+    // loop cost 1-2% per layer)
+    uint32_t bits = 0;
+    auto do_pass = [&](const int ps) {
 #pragma unroll
         for (int q = 0; q < RW; ++q) {
             float acc = 0.0f;
 #pragma unroll
             for (int u = 0; u < PL; ++u)
                 if (u * 64 + lane < NPr) acc = packet_dot_reg<PF>(rc[q][u], 1.0f, hv[u], 0.0f, acc);
-            const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[ps]), q));
+            const float rq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv), q));
             const float v = wave_sum(acc) * rq;
-            const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v[ps]), q));
-            const int row = g + G * (ps * RBP + wv + 4 * q);
+            const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b2v), q));
+            const int row = g + G * (RBP * ps + 4 * q + wv);
+            bool m = false;
             if (row < a.d_ffn) {
                 const bool pre = row < a.kd;  // always-active prefix
                 const float l = pre ? __builtin_inff() : v + bq;
-                const bool m = pre || l > thr;
-                bits[ps] |= (uint32_t)m << q;
+                m = pre || l > thr;
                 if (lane == 0) {
                     if (a.logits) a.logits[row] = l;
                     a.mask[row] = (uint8_t)m;
                 }
             }
+            bits |= (uint32_t)m << (RW * ps + q);
         }
+    };
+    // the first pass in straight-line code (the only one at the smallest
+    // shapes), the rest in a loop
+    do_pass(0);
+    for (int ps = 1; ps < NPS; ++ps) {
+        load_pass(ps);
+        do_pass(ps);
     }
+    if (lane == 0) s_bits[wv] = bits;
     // the group's active rows as one mask over the local index
-    // k = ps * RBP + wv + 4q (ascending k is ascending row g + G*k), built by
-    // every thread from the four waves' bits
-    if (lane == 0) {
-#pragma unroll
-        for (int ps = 0; ps < NPS; ++ps) s_bits[ps][wv] = bits[ps];
-    }
+    // k = RBP ps + 4q + wv (ascending k is ascending row g + G*k), built by
+    // every thread
     __syncthreads();
     unsigned long long act_mask = 0;
-#pragma unroll
-    for (int ps = 0; ps < NPS; ++ps) {
-        const unsigned long long b0 = s_bits[ps][0], b1 = s_bits[ps][1], b2 = s_bits[ps][2],
-                                 b3 = s_bits[ps][3];
-        const int o = ps * RBP;
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-            act_mask |= (((b0 >> q) & 1ull) << (o + 4 * q)) | (((b1 >> q) & 1ull) << (o + 4 * q + 1)) |
-                        (((b2 >> q) & 1ull) << (o + 4 * q + 2)) | (((b3 >> q) & 1ull) << (o + 4 * q + 3));
+    {
+        const uint32_t b0 = s_bits[0], b1 = s_bits[1], b2 = s_bits[2], b3 = s_bits[3];
+        for (int j = 0; j < RW * NPS; ++j)  // j = RW ps + q: local rows 4j .. 4j + 3
+            act_mask |= (unsigned long long)(((b0 >> j) & 1u) | (((b1 >> j) & 1u) << 1) |
+                                             (((b2 >> j) & 1u) << 2) | (((b3 >> j) & 1u) << 3))
+                        << (4 * j);
     }
     const int n_act = __popcll(act_mask);
 
@@ -1026,11 +1011,11 @@ constexpr int layer_b1_waves() {
     return (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
 }
 
-template <int PF, int FMT, bool GATED, int RW, int UA, int UR, bool ADAPT>
+template <int PF, int FMT, bool GATED, int UA, int UR, bool ADAPT>
 __global__ __launch_bounds__(256, (layer_b1_waves<FMT, GATED, UA>())) void layer_b1_kernel(
     FusedArgs f, DownListArgs dn, int slices) {
     if ((int)blockIdx.x < f.groups) {
-        fused_group<PF, FMT, GATED, RW, UA, ADAPT>(f, blockIdx.x);
+        fused_group<PF, FMT, GATED, UA, ADAPT>(f, blockIdx.x);
         return;
     }
     const int q = (int)blockIdx.x - f.groups;
@@ -1198,11 +1183,20 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-int fused_rows_per_group(const Layer &L) {
-    return 4 * (L.desc.w_dtype == SPFFN_Q4_0 ? kFusedRWQ4 * kPassesQ4
-                : L.desc.kind != SPFFN_RELU   ? kFusedRW * kPassesGated
-                                              : kFusedRWNonGated * kPassesNonGated);
+// Rows per pass of a layer's row groups (4 waves x the rows per wave of its
+// instantiation) and W2 passes: about kTargetGroups groups, at least one
+// pass, at most kMaxGroupRows rows.
+static int fused_ua(const Layer &L);
+static int pass_rows(const Layer &L) {
+    return 4 * (L.desc.kind != SPFFN_RELU && fused_ua(L) <= 2 ? 2 : 1);
 }
+int fused_passes(const Layer &L) {
+    const int rp = pass_rows(L);
+    if (rp == 8) return 1;  // two rows per wave: always one pass
+    const int p = (L.desc.d_ffn + rp * kTargetGroups / 2) / (rp * kTargetGroups);
+    return p < 1 ? 1 : p > kMaxGroupRows / rp ? kMaxGroupRows / rp : p;
+}
+int fused_rows_per_group(const Layer &L) { return pass_rows(L) * fused_passes(L); }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
     return (L.desc.d_ffn + RB - 1) / RB;
@@ -1258,32 +1252,31 @@ bool fused_fits(const Layer &L) {
            L.desc.d / packet_elems(L.desc.w_dtype) <= 256 * 8;
 }
 
-template <int PF, int FMT, bool GATED, int RW, int UA, bool ADAPT>
+template <int PF, int FMT, bool GATED, int UA, bool ADAPT>
 static void launch_layer_t(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
                            hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int UR = FMT == kQ4 ? 8 : 16;
     // with timing events the dispatch itself is timestamped (the events bracket
     // the kernel's execution, not its launch)
     if (e0 || e1)
-        hipExtLaunchKernelGGL(layer_b1_kernel<PF, FMT, GATED, RW, UA, UR, ADAPT>, dim3(blocks),
+        hipExtLaunchKernelGGL(layer_b1_kernel<PF, FMT, GATED, UA, UR, ADAPT>, dim3(blocks),
                               dim3(256), 0,
                               s, e0, e1, 0, f, dn, slices);
     else
-        layer_b1_kernel<PF, FMT, GATED, RW, UA, UR, ADAPT><<<blocks, 256, 0, s>>>(f, dn, slices);
+        layer_b1_kernel<PF, FMT, GATED, UA, UR, ADAPT><<<blocks, 256, 0, s>>>(f, dn, slices);
 }
 
 template <int PF, int FMT, bool GATED>
 static void launch_layer_rw(const FusedArgs &f, const DownListArgs &dn, int slices, int blocks,
                             int UA, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr int RW = fused_rw<FMT, GATED>();
     if (f.adapt) {
-        if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2, true>(f, dn, slices, blocks, s, e0, e1);
-        else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4, true>(f, dn, slices, blocks, s, e0, e1);
-        else launch_layer_t<PF, FMT, GATED, RW, 8, true>(f, dn, slices, blocks, s, e0, e1);
+        if (UA == 2) launch_layer_t<PF, FMT, GATED, 2, true>(f, dn, slices, blocks, s, e0, e1);
+        else if (UA == 4) launch_layer_t<PF, FMT, GATED, 4, true>(f, dn, slices, blocks, s, e0, e1);
+        else launch_layer_t<PF, FMT, GATED, 8, true>(f, dn, slices, blocks, s, e0, e1);
     } else {
-        if (UA == 2) launch_layer_t<PF, FMT, GATED, RW, 2, false>(f, dn, slices, blocks, s, e0, e1);
-        else if (UA == 4) launch_layer_t<PF, FMT, GATED, RW, 4, false>(f, dn, slices, blocks, s, e0, e1);
-        else launch_layer_t<PF, FMT, GATED, RW, 8, false>(f, dn, slices, blocks, s, e0, e1);
+        if (UA == 2) launch_layer_t<PF, FMT, GATED, 2, false>(f, dn, slices, blocks, s, e0, e1);
+        else if (UA == 4) launch_layer_t<PF, FMT, GATED, 4, false>(f, dn, slices, blocks, s, e0, e1);
+        else launch_layer_t<PF, FMT, GATED, 8, false>(f, dn, slices, blocks, s, e0, e1);
     }
 }
 
@@ -1323,6 +1316,7 @@ hipError_t launch_layer_b1(const Layer &L, const float *hid, const float *h, con
     f.mask = mask;
     f.lst_i = lst_i;
     f.lst_a = lst_a;
+    f.passes = fused_passes(L);
     f.per_chunk = NG;
     f.done = done;
     DownListArgs dn{};

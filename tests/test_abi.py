@@ -221,7 +221,7 @@ def test_decode_noalloc_rejects_models_beyond_its_array():
     # host-side check, before any HIP call: a model whose workspace exceeds
     # the library's static scratch array is refused with a clear message
     lib = spffn.load()
-    st, h = create(d=8192, d_ffn=1 << 20, r=1024)
+    st, h = create(d=8192, d_ffn=1 << 22, r=1024)
     assert st == OK
     m = C.c_void_p()
     arr = (C.c_void_p * 1)(h.value)
