@@ -23,7 +23,8 @@ def setup_module(module):
 
 
 def _ragged(kind):
-    # fp16 rows, d_ffn = 1003: 8-row groups, the last one has 3 rows
+    # fp16 rows, d_ffn = 1003: 4-row groups (ReLU) or 8-row groups (ReGLU,
+    # two rows per wave at this width), the last one has 3 rows
     return replace(TINY, kind=kind, w_dtype="f16", p_dtype="f16", d=256, d_ffn=1003, r=64)
 
 
@@ -35,11 +36,12 @@ def test_decode_ragged_row_groups(kind, B):
 
 
 def test_decode_most_groups_per_chunk():
-    # d_ffn = 65603: 8201 row groups of 8, so the single-token layer kernel uses
-    # 129 down-projection chunks of 64 groups (the most a chunk's list holds)
-    # and a last chunk of 9 groups
-    print("edge decode 8201 row groups", flush=True)
-    _decode_checks(replace(_ragged("relu"), d_ffn=65603), 1, 2, seed=53)
+    # d_ffn = 170003: row groups of 64 rows (the most a group has), 2657 of
+    # them with a last group of 19 rows, so the single-token layer kernel's
+    # 133 down-projection chunks hold 20 groups each (1280 list slots, the
+    # most a chunk's list holds) and the last chunk 17 groups
+    print("edge decode 2657 row groups of 64", flush=True)
+    _decode_checks(replace(_ragged("relu"), d_ffn=170003), 1, 2, seed=53)
 
 
 def test_layer_kernel_wait_gives_up_with_nan():
