@@ -501,7 +501,8 @@ struct FusedArgs {
 // previous pass's are multiplied), so a group costs the registers of one pass
 // whatever its size.  P is chosen per layer (fused_passes) so that the layer
 // has about kTargetGroups row groups -- four per CU of the 256 CUs: one round
-// of resident workgroups, with a slot per CU left to the down workgroups --
+// of resident workgroups (at five waves per SIMD with a slot per CU left to
+// the down workgroups) --
 // and a group at most 64 rows (its list slots are written by its first wave).
 // Found by sweeping fixed group sizes per layer of a decode step (us), against
 // the best one-pass groups: 175B-shaped 4-bit rows, 48 rows (12 passes) 52.1
@@ -658,12 +659,14 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     // zero activation values, so every load is unconditional.
     float xv[UA][E], xs[UA];
     unsigned long long pending = act_mask;
-    // Non-gated fp16 and fp32 rows: the group's active rows two at a time,
-    // both rows' loads in flight together (32-row groups hold ~2.5 active
-    // rows at the 40B shape: 40.4 -> 39.4 us per layer).  4-bit rows keep
-    // one row at a time: their 64 activation values per lane leave no room
-    // for a second row without spills (52.2 -> 62.2 us at the 175B shape).
-    if constexpr (!GATED && FMT != kQ4) {
+    // fp16 and fp32 rows: the group's active rows two at a time, both rows'
+    // loads in flight together (non-gated 32-row groups hold ~2.5 active rows
+    // at the 40B shape: 40.4 -> 39.4 us per layer; gated 28-row groups ~2.8 at
+    // the 70B shape, whose kernel then runs at four waves per SIMD: step 3.622
+    // -> 3.599 ms; 7B 0.790 -> 0.776).  Gated rows wider than 8192 columns and
+    // 4-bit rows keep one row at a time: a second row's registers beside the
+    // lane's activation values spill (4-bit: 52.2 -> 62.2 us at the 175B shape).
+    if constexpr (FMT != kQ4 && (!GATED || UA <= 4)) {
         for (int k = 0; k < n_act; k += 2) {
             const int kl0 = __ffsll(pending) - 1;
             pending &= pending - 1;
@@ -674,14 +677,18 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
                 pending &= pending - 1;
             }
             const int i0 = g + G * kl0, i1 = g + G * kl1;
-            uint4 ra[UA], rb[UA];
-            float sa[UA], sb[UA];
+            uint4 ra[UA], rb[UA], ua[UA], ub[UA];
+            float sa[UA], sb[UA], sua[UA], sub[UA];
 #pragma unroll
             for (int u = 0; u < UA; ++u) {
                 const int p = wv * 64 + lane + 256 * u;
                 const int pc = p < NPd ? p : NPd - 1;
                 ra[u] = ld_stream(row_ptr<FMT>(a.wa, i0, a.d) + pc);
                 sa[u] = packet_scale<FMT>(a.wa, i0, a.d, pc);
+                if constexpr (GATED) {
+                    ua[u] = ld_stream(row_ptr<FMT>(a.wu, i0, a.d) + pc);
+                    sua[u] = packet_scale<FMT>(a.wu, i0, a.d, pc);
+                }
             }
             if (two) {
 #pragma unroll
@@ -690,12 +697,18 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
                     const int pc = p < NPd ? p : NPd - 1;
                     rb[u] = ld_stream(row_ptr<FMT>(a.wa, i1, a.d) + pc);
                     sb[u] = packet_scale<FMT>(a.wa, i1, a.d, pc);
+                    if constexpr (GATED) {
+                        ub[u] = ld_stream(row_ptr<FMT>(a.wu, i1, a.d) + pc);
+                        sub[u] = packet_scale<FMT>(a.wu, i1, a.d, pc);
+                    }
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < UA; ++u) {
                     rb[u] = make_uint4(0, 0, 0, 0);
                     sb[u] = 0.0f;
+                    ub[u] = make_uint4(0, 0, 0, 0);
+                    sub[u] = 0.0f;
                 }
             }
             if (k == 0) {
@@ -715,20 +728,28 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
                         xs[u] = 0.0f;
                     }
             }
-            float za = 0.0f, zb = 0.0f;
+            float za = 0.0f, zb = 0.0f, zua = 0.0f, zub = 0.0f;
 #pragma unroll
             for (int u = 0; u < UA; ++u) {
                 za = packet_dot_reg<FMT>(ra[u], sa[u], xv[u], xs[u], za);
                 zb = packet_dot_reg<FMT>(rb[u], sb[u], xv[u], xs[u], zb);
+                if constexpr (GATED) {
+                    zua = packet_dot_reg<FMT>(ua[u], sua[u], xv[u], xs[u], zua);
+                    zub = packet_dot_reg<FMT>(ub[u], sub[u], xv[u], xs[u], zub);
+                }
             }
             za = wave_sum(za);
             zb = wave_sum(zb);
+            if constexpr (GATED) {
+                zua = wave_sum(zua);
+                zub = wave_sum(zub);
+            }
             if (lane == 0) {
                 s_part[k][wv][0] = za;
-                s_part[k][wv][1] = 0.0f;
+                s_part[k][wv][1] = zua;
                 if (two) {
                     s_part[k + 1][wv][0] = zb;
-                    s_part[k + 1][wv][1] = 0.0f;
+                    s_part[k + 1][wv][1] = zub;
                 }
             }
         }
@@ -1004,11 +1025,14 @@ static std::atomic<int> g_chunk_wait_polls{kChunkWaitPollsDefault};
 
 void set_chunk_wait_polls(int polls) { g_chunk_wait_polls.store(polls); }
 
-// Five resident waves per SIMD where the registers allow it without spills
-// (wider rows and gated 4-bit rows keep the compiler's own budget).
+// Five resident waves per SIMD where the registers allow it without spills;
+// gated fp16 / fp32 rows of 4097-8192 columns four (their pairs of gathered
+// rows need 108 VGPRs; with about 1024 row groups, four per CU, they still
+// fit one round); wider rows and gated 4-bit rows keep the compiler's own
+// budget.
 template <int FMT, bool GATED, int UA>
 constexpr int layer_b1_waves() {
-    return (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
+    return (FMT != kQ4 && GATED && UA == 4) ? 4 : (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
 }
 
 template <int PF, int FMT, bool GATED, int UA, int UR, bool ADAPT>
