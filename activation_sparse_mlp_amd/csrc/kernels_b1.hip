@@ -659,14 +659,15 @@ __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     // zero activation values, so every load is unconditional.
     float xv[UA][E], xs[UA];
     unsigned long long pending = act_mask;
-    // fp16 and fp32 rows: the group's active rows two at a time, both rows'
-    // loads in flight together (non-gated 32-row groups hold ~2.5 active rows
-    // at the 40B shape: 40.4 -> 39.4 us per layer; gated 28-row groups ~2.8 at
-    // the 70B shape, whose kernel then runs at four waves per SIMD: step 3.622
-    // -> 3.599 ms; 7B 0.790 -> 0.776).  Gated rows wider than 8192 columns and
-    // 4-bit rows keep one row at a time: a second row's registers beside the
-    // lane's activation values spill (4-bit: 52.2 -> 62.2 us at the 175B shape).
-    if constexpr (FMT != kQ4 && (!GATED || UA <= 4)) {
+    // The group's active rows two at a time, both rows' loads in flight
+    // together: non-gated fp16 32-row groups hold ~2.5 active rows at the 40B
+    // shape (40.4 -> 39.4 us per layer); gated fp16 28-row groups ~2.8 at the
+    // 70B shape and 4-bit 48-row groups ~2.5 at the 175B shape, whose kernels
+    // then run at four waves per SIMD for the pair's registers (steps 3.622 ->
+    // 3.599 ms and 5.121 -> 5.043 ms; 7B 0.790 -> 0.776; at five waves the
+    // 4-bit pair spilled, 52.2 -> 62.2 us per layer).  Gated rows wider than
+    // 8192 columns and gated 4-bit rows keep one row at a time.
+    if constexpr ((FMT != kQ4 && (!GATED || UA <= 4)) || (FMT == kQ4 && !GATED && UA == 2)) {
         for (int k = 0; k < n_act; k += 2) {
             const int kl0 = __ffsll(pending) - 1;
             pending &= pending - 1;
@@ -1026,13 +1027,13 @@ static std::atomic<int> g_chunk_wait_polls{kChunkWaitPollsDefault};
 void set_chunk_wait_polls(int polls) { g_chunk_wait_polls.store(polls); }
 
 // Five resident waves per SIMD where the registers allow it without spills;
-// gated fp16 / fp32 rows of 4097-8192 columns four (their pairs of gathered
-// rows need 108 VGPRs; with about 1024 row groups, four per CU, they still
-// fit one round); wider rows and gated 4-bit rows keep the compiler's own
-// budget.
+// gated fp16 / fp32 rows of 4097-8192 columns and non-gated 4-bit rows four
+// (their pairs of gathered rows need 105-108 VGPRs; with about 1024 row
+// groups, four per CU, they still fit one round); wider rows and gated 4-bit
+// rows keep the compiler's own budget.
 template <int FMT, bool GATED, int UA>
 constexpr int layer_b1_waves() {
-    return (FMT != kQ4 && GATED && UA == 4) ? 4 : (FMT != kQ4 && UA <= 4) || (FMT == kQ4 && !GATED && UA == 2) ? 5 : 1;
+    return (FMT != kQ4 && GATED && UA == 4) || (FMT == kQ4 && !GATED && UA == 2) ? 4 : (FMT != kQ4 && UA <= 4) ? 5 : 1;
 }
 
 template <int PF, int FMT, bool GATED, int UA, int UR, bool ADAPT>
