@@ -517,31 +517,25 @@ struct FusedArgs {
 // vs 2.336, 7B 0.781 vs 0.775, 175B 5.123 vs 5.099.
 constexpr int kTargetGroups = 1024;
 constexpr int kMaxGroupRows = 64;
-// Rows per wave in a pass: one, except gated rows of at most 4096 columns
-// (UA <= 2, the 7B shape), whose small layers read two rows per wave in one
-// pass -- both rows in flight together, 8-row groups: 7B-shaped step 0.770 ms
-// against 0.785 for 12-row groups in three one-row passes and 0.783 for
-// 8-row groups in two.
-template <bool GATED, int UA> constexpr int pass_rows_per_wave() { return GATED && UA <= 2 ? 2 : 1; }
-// (The one-pass case must stay a compile-time constant: with the pass count
-// read from the arguments the 7B-shaped step took 0.785 ms against 0.772.)
+// One row per wave in a pass.  (Small gated layers did better with 8-row
+// groups in one pass of two rows per wave until their active rows were
+// gathered in pairs; since then 12-row groups in three passes are faster at
+// the 7B shape: 0.773 against 0.778 ms per step.)
+constexpr int kPassRowsPerWave = 1;
 
 template <int PF, int FMT, bool GATED, int UA, bool ADAPT>
 __device__ __forceinline__ void fused_group(const FusedArgs &a, const int g) {
     constexpr int EP = PacketElems<PF>::value;
     constexpr int E = PacketElems<FMT>::value;
     constexpr int PL = PF == kFP8 ? 1 : 2;  // W2 packets per lane per row (one pass)
-    constexpr int RW = pass_rows_per_wave<GATED, UA>();
+    constexpr int RW = kPassRowsPerWave;
     constexpr int RBP = 4 * RW;  // rows per pass
-    constexpr int RBMAX = RW == 2 ? RBP : kMaxGroupRows;  // rows per group at most
     __shared__ uint32_t s_bits[4];
-    __shared__ float s_bias[RBMAX];  // bias of every row of the group, by local index
-    __shared__ float s_part[RBMAX][4][2];
+    __shared__ float s_bias[kMaxGroupRows];  // bias of every row of the group, by local index
+    __shared__ float s_part[kMaxGroupRows][4][2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int G = a.groups;
-    // W2 passes; row k = RBP ps + 4q + wv of the group in pass ps (always one
-    // pass with two rows per wave)
-    const int NPS = RW == 2 ? 1 : a.passes;
+    const int NPS = a.passes;  // W2 passes; row k = RBP ps + 4q + wv of the group in pass ps
     const int RB = RBP * NPS;  // rows per row group (one group per workgroup)
     const int NPr = a.r / EP, NPd = a.d / E;
 
@@ -1208,20 +1202,14 @@ hipError_t launch_down_b1(const Layer &L, const int32_t *idx, const int32_t *cou
     return hipGetLastError();
 }
 
-// Rows per pass of a layer's row groups (4 waves x the rows per wave of its
-// instantiation) and W2 passes: about kTargetGroups groups, at least one
-// pass, at most kMaxGroupRows rows.
-static int fused_ua(const Layer &L);
-static int pass_rows(const Layer &L) {
-    return 4 * (L.desc.kind != SPFFN_RELU && fused_ua(L) <= 2 ? 2 : 1);
-}
+// W2 passes of a layer's row groups (4 waves x kPassRowsPerWave rows each):
+// about kTargetGroups groups, at least one pass, at most kMaxGroupRows rows.
 int fused_passes(const Layer &L) {
-    const int rp = pass_rows(L);
-    if (rp == 8) return 1;  // two rows per wave: always one pass
+    constexpr int rp = 4 * kPassRowsPerWave;
     const int p = (L.desc.d_ffn + rp * kTargetGroups / 2) / (rp * kTargetGroups);
     return p < 1 ? 1 : p > kMaxGroupRows / rp ? kMaxGroupRows / rp : p;
 }
-int fused_rows_per_group(const Layer &L) { return pass_rows(L) * fused_passes(L); }
+int fused_rows_per_group(const Layer &L) { return 4 * kPassRowsPerWave * fused_passes(L); }
 int fused_groups(const Layer &L) {
     const int RB = fused_rows_per_group(L);
     return (L.desc.d_ffn + RB - 1) / RB;

@@ -23,8 +23,7 @@ def setup_module(module):
 
 
 def _ragged(kind):
-    # fp16 rows, d_ffn = 1003: 4-row groups (ReLU) or 8-row groups (ReGLU,
-    # two rows per wave at this width), the last one has 3 rows
+    # fp16 rows, d_ffn = 1003: 4-row groups (one pass), the last one has 3 rows
     return replace(TINY, kind=kind, w_dtype="f16", p_dtype="f16", d=256, d_ffn=1003, r=64)
 
 
