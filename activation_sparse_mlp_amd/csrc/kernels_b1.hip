@@ -5,7 +5,7 @@
 // Decode step, per layer (three kernels):
 //   w1x_b1       hid = ReLU((W1 . h) * s + b1), s = 1/sqrt(mean(h^2) + eps)
 //   layer_b1     row groups: logit = W2 . hid + b2, mask = logit > t, and for
-//                the active rows of each 8-row group act = max(z, 0) [* u]
+//                the active rows of each row group act = max(z, 0) [* u]
 //                with z = (W_act[i] . h) * s + b_i, listed per group;
 //                down workgroups (same launch, once a chunk's groups are
 //                done): part[c, slice] = sum over the lists of chunk c of
@@ -449,10 +449,11 @@ __global__ __launch_bounds__(256) void reduce_groups_kernel(const float *__restr
 // chunk of NG consecutive row groups).
 //
 // Row group g owns the interleaved W2 rows {g + G*k : k < RB}, so the
-// hot-first rows spread one per group.  It computes their logits, writes the
-// mask, lists its active rows in LDS (ascending within the group), computes
-// the activation of each listed row with all four waves sharing the row's
-// packets, and writes the RB slots [g*RB, g*RB + RB) of lst_i / lst_a
+// hot-first rows spread one per group.  It computes their logits in passes
+// of one row per wave, writes the mask, keeps its active rows as a register
+// mask (ascending within the group), computes the activation of each active
+// row with all four waves sharing the row's packets (two rows at a time for
+// most row kinds), and writes the RB slots [g*RB, g*RB + RB) of lst_i / lst_a
 // (neuron, activation; its active rows first, the rest neuron -1).  It then
 // publishes them: the slots are written with agent-scope (L2-coherent)
 // stores, and once they have completed, done[c] of its chunk c = g / NG is
