@@ -15,7 +15,7 @@ import activation_sparse_mlp_amd as spffn
 import oracle
 from tests.gpu_helpers import DEV, REL_L2, check_mask_agreement, gpu_layer, np_layer, rel_l2
 from tests.test_gpu_mixed import CFGS as MIXED
-from workloads import LLAMA2_7B, TINY, make_layer, make_tokens
+from workloads import LLAMA2_7B, OPT_175B_Q4, TINY, make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,10 @@ def setup_module(module):
 
 _F16 = replace(LLAMA2_7B, d=512, d_ffn=1536, r=64)        # fp16 rows, vector path at B > 1
 _MF = replace(LLAMA2_7B, d=4096, d_ffn=1000, r=512)       # matrix cores at B > 1
+# single-token layer kernels whose row groups read their predictor rows in
+# four passes (16-row groups, about 1024 of them) and gather in pairs
+_F16_PASSES = replace(LLAMA2_7B, d=512, d_ffn=16384, r=64)
+_Q4_PASSES = replace(OPT_175B_Q4, d=512, d_ffn=16390, r=64, layers=2)
 
 
 def _check(cfgs, B, seed):
@@ -81,6 +85,8 @@ def _check(cfgs, B, seed):
 @pytest.mark.parametrize("cfg,B", [
     (TINY, 1),      # fp32 rows, single-token layer kernel
     (_F16, 1),      # fp16 rows, single-token layer kernel
+    (_F16_PASSES, 1),  # fp16 rows, row groups in four passes
+    (_Q4_PASSES, 1),   # 4-bit rows, row groups in four passes
     (_F16, 3),      # batched vector path
     (_MF, 4),       # matrix cores, tokens sharing one instruction
     (_MF, 11),      # matrix cores, two instructions per tile
