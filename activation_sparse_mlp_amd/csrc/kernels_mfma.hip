@@ -418,21 +418,31 @@ __global__ __launch_bounds__(256) void w1_finish_kernel(const float *__restrict_
                                                         float *__restrict__ tsc) {
     __shared__ float red[4];
     const int b = blockIdx.y;
+    // The K-split partial sums are requested before the RMS sums are reduced
+    // (independent loads, one round trip instead of two; 70B layer at B = 4
+    // 100.7 -> 99.1 us, B = 16 173.3 -> 171.5, 40B at B = 8 113.6 -> 112.1).
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t t = (size_t)b * r + i;
+    constexpr int KMAX = 8;
+    float pv[KMAX];
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) pv[c] = (i < r && c < KS) ? part[(size_t)c * B * r + t] : 0.0f;
     float s = 1.0f;
     if (ss) {
         float q = 0.0f;
-        for (int i = threadIdx.x; i < nss; i += blockDim.x) q += ss[(size_t)b * nss + i];
+        for (int k = threadIdx.x; k < nss; k += blockDim.x) q += ss[(size_t)b * nss + k];
         q = wave_sum(q);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = q;
         __syncthreads();
         s = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) * inv_k + eps);
         if (blockIdx.x == 0 && threadIdx.x == 0 && tsc) tsc[b] = s;
     }
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < r) {
-        const size_t t = (size_t)b * r + i;
-        float v = 0.0f;
-        for (int c = 0; c < KS; ++c) v += part[(size_t)c * B * r + t];
+        float v = 0.0f;  // the splits in ascending order
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c)
+            if (c < KS) v += pv[c];
+        for (int c = KMAX; c < KS; ++c) v += part[(size_t)c * B * r + t];
         v = fmaxf(fmaf(v, s, b1 ? b1[i] : 0.0f), 0.0f);
         hid[t] = v;
         bpack_store(hhi, hlo, B, b, i, v);
